@@ -1,0 +1,232 @@
+"""Benchmark: MoE layout -> dispatch -> combine on one MI355X.
+
+One step = one pass of the whole path over one batch: ep_layout (counts,
+offsets, stable slots), ep_dispatch (FP8 E4M3 1x128 quantise + copy for the
+V3 shape), ep_combine (weighted BF16 reduction of the expert outputs). The
+expert computation between dispatch and combine is not part of this path;
+combine reads a seeded synthetic expert output of the receive layout.
+
+Inputs are seeded synthetic data resident in HBM before the timed region.
+Throughput is algorithmic bytes (the minimum each kernel must read and
+write) over time; `roofline` reports the dominant kernel against the
+MI355X HBM peak, timed with HIP events on the stream the kernels run on.
+`cpu_baseline` times the single-threaded CPU oracle on the same inputs.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch/combine effective GB/s + % of HBM peak, 8K tok×7168 top-8"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_device.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="v3")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    return p.parse_args()
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "combine_ep_layout_10_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, R: int, P: int, dispatch: str) -> dict:
+    """Minimum bytes each kernel must move (MB = 1e6 B in reports)."""
+    T, H, k = wl.T, wl.H, wl.k
+    nb = H // 128
+    if dispatch == "fp8":
+        row_out = H + 4 * nb            # codes + 1x128 scales
+    else:
+        row_out = 2 * H
+    pad_rows = max(R - P, 0) if wl.mode == 0 else 0
+    layout = T * k * 8 + T * k * 4 + T * k * 4 + 2 * 4 * (R if wl.mode == 0 else P)
+    dispatch_b = T * H * 2 + T * k * 4 + P * row_out + pad_rows * row_out
+    combine = P * H * 2 + T * k * 4 + T * k * 4 + T * H * 2
+    return {"layout": layout, "dispatch": dispatch_b, "combine": combine,
+            "padding_rows": pad_rows, "pairs": P, "rows": R}
+
+
+def load_traffic(kernel: str, khash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel)
+    if not ent or ent.get("kernel_hash") != khash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested). Run with --gpus 1." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from ep_workloads import WORKLOADS, make_inputs, draw_routing, draw_weights, draw_hidden, _streams
+    from combine_ep_layout_10_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
+    sx, sr, sl, so, sy = _streams(0)
+    x_h = draw_hidden(wl, sx, so)
+    idx_h = draw_routing(wl, sr)
+    w_h = draw_weights(wl, sl)
+    cfg = ops.Config(max_tokens=wl.T, hidden=wl.H, num_experts=wl.E, num_topk=wl.k, num_dests=wl.D,
+                     expert_alignment=wl.A, capacity=wl.C, mode=wl.mode, idx_bits=64)
+    R_cap = cfg.recv_rows_bound()
+    x = torch.from_numpy(x_h.view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(idx_h).to(dev)
+    w = torch.from_numpy(w_h).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    y = torch.randn((R_cap, wl.H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ws = ops.new_workspace(cfg, dev)
+    fp8 = wl.dispatch == "fp8"
+    dtype = ops.FP8_QUANTIZE if fp8 else ops.BF16
+    recv = torch.empty((R_cap, wl.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    rs = torch.empty((R_cap, wl.H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        h = ops.layout(cfg, idx, w, workspace=ws)
+        if evs:
+            evs[1].record(stream)
+        if fp8:
+            ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs)
+        else:
+            ops.dispatch(h, x, dtype, recv=recv)
+        if evs:
+            evs[2].record(stream)
+        ops.combine(h, y, w, out=out)
+        if evs:
+            evs[3].record(stream)
+        return h
+
+    h = step()
+    cnt, pad, R = h.read_counts()
+    flags = h.check()
+    if flags:
+        raise RuntimeError("layout raised error flags %d on a valid workload" % flags)
+    P = int(cnt.sum()) if wl.mode == 0 else int(pad.sum())
+    nbytes = algorithmic_bytes(wl, R, P, wl.dispatch)
+    step_bytes = nbytes["layout"] + nbytes["dispatch"] + nbytes["combine"]
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    lay_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dis_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    com_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    gpu_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    khash = kernel_hash()
+    com_gbps = nbytes["combine"] / (com_ms * 1e-3) / 1e9
+    dis_gbps = nbytes["dispatch"] / (dis_ms * 1e-3) / 1e9
+    dominant = "combine" if nbytes["combine"] >= nbytes["dispatch"] else "dispatch"
+    dom_gbps = com_gbps if dominant == "combine" else dis_gbps
+    traffic = load_traffic("k_combine" if dominant == "combine" else "k_dispatch", khash)
+    roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "k_combine<true>" if dominant == "combine" else "k_dispatch",
+                "algorithmic_bytes_per_launch": nbytes[dominant],
+                "avg_launch_us": round((com_ms if dominant == "combine" else dis_ms) * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        times = []
+        budget_end = time.perf_counter() + args.cpu_budget_s
+        while not times or (len(times) < 3 and time.perf_counter() < budget_end):
+            c0 = time.perf_counter()
+            lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, idx_h, w_h)
+            if fp8:
+                oracle.dispatch_fp8(lay, x_h, wl.k)
+            else:
+                oracle.dispatch_bf16(lay, x_h, wl.k)
+            oracle.combine(lay, y_h, wl.k, w_h)
+            times.append(time.perf_counter() - c0)
+            print("[bench] oracle step %.2f s" % times[-1], file=sys.stderr, flush=True)
+        cpu_s = float(np.median(times))
+        cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the full %s step (layout + %s dispatch + combine) on the same inputs, median of %d "
+                         "runs of %.2f s; single-threaded C oracle" % (wl.name, wl.dispatch, len(times), cpu_s)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
+                   "expert_alignment": wl.A, "dests": wl.D, "mode": "fixed" if wl.mode else "compact",
+                   "dispatch": "fp8_e4m3_1x128" if fp8 else "bf16", "combine": "bf16", "routing": wl.routing},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {
+            "layout_us": round(lay_ms * 1e3, 2), "dispatch_us": round(dis_ms * 1e3, 2),
+            "combine_us": round(com_ms * 1e3, 2), "gpu_step_us": round(gpu_ms * 1e3, 2),
+            "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
+            "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
+            "bytes": nbytes, "kernel_hash": khash,
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

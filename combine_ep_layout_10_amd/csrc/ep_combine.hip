@@ -1,0 +1,88 @@
+// Combine kernel: reduce each token's k expert-output rows back into one
+// BF16 row — the DeepEP README's combine_forward, and dispatch_backward (a
+// combine without weights that also gathers per-row values back to the
+// pairs), for the receive rows of one GPU.
+//
+// One block per token; each lane owns 8 channels (one dwordx4 of bf16) of
+// the output row. It issues the loads of all k source rows (up to 8 at a
+// time) before any arithmetic, so k 16-byte loads per lane are in flight,
+// then accumulates in binary32 with fused multiply-add in k order from +0,
+// rounds to bf16 (nearest even) and writes one dwordx4.
+#include "ep_internal.h"
+
+namespace ep {
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // Lane j < k of every wave holds pair j's slot and weight; the loops below
+    // broadcast them with readlane, so no load sits between the row loads.
+    int my_s = -1;
+    float my_w = 0.0f;
+    if (lane < a.k) {
+        my_s = a.slot[(int64_t)t * a.k + lane];
+        if (WEIGHTED) my_w = a.w[(int64_t)t * a.k + lane];
+    }
+    if (a.out_vals != nullptr && tid < a.k)
+        a.out_vals[(int64_t)t * a.k + tid] = my_s >= 0 ? a.row_vals[my_s] : 0.0f;
+
+    const int nvec = a.H / 8;
+    for (int c = tid; c < nvec; c += blockDim.x) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {
+            uint4 v[8];
+            int s[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s[u] = j0 + u < a.k ? __builtin_amdgcn_readlane(my_s, j0 + u) : -1;
+                v[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (s[u] >= 0) v[u] = ((const uint4*)(a.y + (int64_t)s[u] * a.H))[c];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (s[u] < 0) continue;
+                float f[8];
+                f[0] = bf16_to_f32(v[u].x & 0xFFFFu);
+                f[1] = bf16_to_f32(v[u].x >> 16);
+                f[2] = bf16_to_f32(v[u].y & 0xFFFFu);
+                f[3] = bf16_to_f32(v[u].y >> 16);
+                f[4] = bf16_to_f32(v[u].z & 0xFFFFu);
+                f[5] = bf16_to_f32(v[u].z >> 16);
+                f[6] = bf16_to_f32(v[u].w & 0xFFFFu);
+                f[7] = bf16_to_f32(v[u].w >> 16);
+                if (WEIGHTED) {
+                    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j0 + u));
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
+                }
+            }
+        }
+        uint4 o;
+        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+        o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+        ((uint4*)(a.out + (int64_t)t * a.H))[c] = o;
+    }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int nvec = a.H / 8;
+    int threads = ((nvec + 63) / 64) * 64;
+    if (threads > 1024) threads = 1024;
+    if (threads < 64) threads = 64;
+    if (a.w != nullptr)
+        hipLaunchKernelGGL(k_combine<true>, dim3(a.T), dim3(threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_combine<false>, dim3(a.T), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,112 @@
+// Device helpers shared by the gfx950 kernels of the dispatch/combine library.
+// Wave64 only: every lane mask below is 64 bits wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// binary32 -> bfloat16 bits, round to nearest even. Inputs are finite: adding
+// 0x7FFF plus the kept LSB carries into the kept half exactly when the
+// discarded half is above one half, or equal to it with an odd kept LSB.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// binary32 -> OCP E4M3FN byte, round to nearest even, saturating at +-448.
+// |v| >= 2^-6 (normal E4M3): the E4M3 code of a normal value is the binary32
+// pattern's exponent rebiased (127 -> 7) followed by its top three mantissa
+// bits, so rounding the pattern at bit 20 (RNE on the integer) and
+// subtracting the bias difference (120 << 3) gives the code, with mantissa
+// carries stepping the exponent. |v| < 2^-6: the E4M3 subnormals are
+// m * 2^-9, so the code is |v| * 512 rounded to the nearest even integer
+// (0..8; 8 is the smallest normal 0x08). Codes above 0x7E (448) saturate.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    float af = __uint_as_float(a);
+    uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t sub = (uint32_t)__builtin_rintf(af * 512.0f);
+    uint32_t code = af < 0.015625f ? sub : normal;
+    code = code > 0x7Eu ? 0x7Eu : code;
+    return sign | code;
+}
+
+// ---------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Lanes of the wave whose (active, key) equals this lane's: AND over the key's
+// bits of "lanes that agree on this bit". nbits covers every key value.
+__device__ __forceinline__ uint64_t match_peers(int key, bool active, int nbits) {
+    uint64_t m = ballot64(active);
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (key >> b) & 1;
+        uint64_t on = ballot64(active && bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Max over the 8 consecutive lanes of an aligned group (lane & ~7) with DPP:
+// swap neighbours, swap pairs, then mirror inside each half-row of 8.
+__device__ __forceinline__ float max8_dpp(float v) {
+    int x = __float_as_int(v);
+    int y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(y));
+    x = __float_as_int(v);
+    y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(y));
+    x = __float_as_int(v);
+    y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);      // row_half_mirror
+    return fmaxf(v, __int_as_float(y));
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a block of nthreads (multiple of 64, <= 1024).
+// `tmp` is LDS of at least 17 ints. Every thread of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    int inc = wave_inclusive_scan(v);
+    if (lane == 63) tmp[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        int s = lane < nw ? tmp[lane] : 0;
+        int si = wave_inclusive_scan(s);
+        if (lane < nw) tmp[lane] = si - s;
+        if (lane == nw - 1) tmp[16] = si;
+    }
+    __syncthreads();
+    int out = inc - v + tmp[w];
+    *total = tmp[16];
+    __syncthreads();
+    return out;
+}
+
+}  // namespace ep

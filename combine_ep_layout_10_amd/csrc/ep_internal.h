@@ -1,0 +1,80 @@
+// Kernel argument blocks and launch entry points of the HIP library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ep.h"
+#include "ep_device.h"
+
+namespace ep {
+
+// Multi-block layout: waves per block and groups of 64 pairs per wave.
+constexpr int kLayoutWaves = 4;
+constexpr int kLayoutIters = 8;
+constexpr int kLayoutPairsPerBlock = kLayoutWaves * kLayoutIters * kWave;  // 2048
+// Single-block layout limits.
+constexpr int kSmallMaxPairs = 4096;
+constexpr int kSmallMaxExperts = 512;
+// Limits checked by the host API.
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 32;
+
+struct LayoutArgs {
+    const void* idx;
+    const float* w;
+    int idx_bits;
+    int T, E, k, A, D, C, mode;
+    int nbits;  // bits needed to hold any expert id
+    int epd;    // experts per destination
+    int nblk;   // multi-block grid size
+    int32_t* cnt;
+    int32_t* pad;
+    int32_t* expert_off;
+    int32_t* dest_off;
+    int32_t* dest_tokens;
+    int32_t* slot;
+    int32_t* row_src;
+    float* row_w;
+    uint32_t* err_flags;
+    int32_t* bpart;   // [nblk][E] per-block counts, then per-block bases
+    int32_t* dpart;   // [nblk][D] per-block distinct-token counts
+    uint32_t* fpart;  // [nblk] per-block error bits
+};
+
+enum DispatchKind { kDispatchBf16 = 0, kDispatchBf16Weighted = 1, kDispatchFp8Quant = 2, kDispatchFp8Copy = 3 };
+
+struct DispatchArgs {
+    const void* x;
+    const float* x_scales;
+    void* recv;
+    float* recv_scales;
+    const int32_t* slot;
+    const float* pair_w;
+    const int32_t* cnt;
+    const int32_t* pad;
+    const int32_t* expert_off;
+    int T, H, k, E;
+    int zero_pad;
+    int pad_blocks_per_expert;
+    int npad_blocks;
+};
+
+struct CombineArgs {
+    const uint16_t* y;
+    const float* w;
+    uint16_t* out;
+    const int32_t* slot;
+    const float* row_vals;
+    float* out_vals;
+    int T, H, k;
+};
+
+// Rows of padding one dispatch block clears.
+constexpr int kPadRowsPerBlock = 16;
+
+hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
+hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace ep

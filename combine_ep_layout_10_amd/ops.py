@@ -1,0 +1,245 @@
+"""Torch-facing calls over the C ABI: PyTorch supplies device memory and the
+stream, every step runs in the HIP kernels behind include/ep.h.
+
+Mapping to the DeepEP README ("Interfaces and examples"):
+  layout + dispatch            -> dispatch_forward (recv_x, handle)
+  Handle.row_src / row_w       -> recv_topk_idx / recv_topk_weights (per row)
+  Handle.pad (read_counts)     -> handle.num_recv_tokens_per_expert_list
+  combine                      -> combine_forward
+  dispatch_backward            -> dispatch_backward (a combine)
+  combine_backward             -> combine_backward (a dispatch on the handle)
+  dispatch with an old Handle  -> decode_dispatch with cached_handle
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _ffi as F
+
+MODE_COMPACT = F.EP_MODE_COMPACT
+MODE_FIXED = F.EP_MODE_FIXED
+BF16 = F.EP_BF16
+FP8_QUANTIZE = F.EP_FP8_QUANTIZE
+FP8_PREQUANT = F.EP_FP8_PREQUANT
+FLAG_NO_ZERO_PAD = F.EP_FLAG_NO_ZERO_PAD
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    max_tokens: int
+    hidden: int
+    num_experts: int
+    num_topk: int
+    num_dests: int = 1
+    expert_alignment: int = 1
+    capacity: int = 0
+    mode: int = MODE_COMPACT
+    idx_bits: int = 64
+    flags: int = 0
+
+    def c(self) -> F.ep_config:
+        return F.ep_config(self.max_tokens, self.hidden, self.num_experts, self.num_topk, self.num_dests,
+                           self.expert_alignment, self.capacity, self.mode, self.idx_bits, self.flags)
+
+    def workspace_bytes(self) -> int:
+        n = F.ep_workspace_bytes(self.c())
+        if n == 0:
+            raise F.EPError(F.EP_ERR_INVALID_ARG, "ep_workspace_bytes", F.last_error_message())
+        return n
+
+    def recv_rows_bound(self) -> int:
+        n = F.ep_recv_rows_bound(self.c())
+        if n < 0:
+            raise F.EPError(F.EP_ERR_INVALID_ARG, "ep_recv_rows_bound", F.last_error_message())
+        return n
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return t.data_ptr()
+
+
+def _opt(t: Optional[torch.Tensor], name: str, dtype=None):
+    return None if t is None else _dev(t, name, dtype)
+
+
+def _need(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """The kernels index these buffers by the handle's sizes: check them here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class Handle:
+    """An ep_handle plus the workspace tensor it points into."""
+
+    def __init__(self, cfg: Config, h: F.ep_handle, workspace: torch.Tensor):
+        self.cfg = cfg
+        self.c = h
+        self.workspace = workspace
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.c.num_tokens)
+
+    def _view(self, ptr: int, n: int, dtype) -> torch.Tensor:
+        off = ptr - self.workspace.data_ptr()
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off: off + n * itemsize].view(dtype)
+
+    @property
+    def cnt(self):
+        return self._view(self.c.cnt, self.cfg.num_experts, torch.int32)
+
+    @property
+    def pad(self):
+        return self._view(self.c.pad, self.cfg.num_experts, torch.int32)
+
+    @property
+    def expert_off(self):
+        return self._view(self.c.expert_off, self.cfg.num_experts + 1, torch.int32)
+
+    @property
+    def dest_off(self):
+        return self._view(self.c.dest_off, self.cfg.num_dests + 1, torch.int32)
+
+    @property
+    def dest_tokens(self):
+        return self._view(self.c.dest_tokens, self.cfg.num_dests, torch.int32)
+
+    @property
+    def slot(self):
+        return self._view(self.c.slot, self.num_tokens * self.cfg.num_topk, torch.int32)
+
+    @property
+    def row_src(self):
+        return self._view(self.c.row_src, self.cfg.recv_rows_bound(), torch.int32)
+
+    @property
+    def row_w(self):
+        return self._view(self.c.row_w, self.cfg.recv_rows_bound(), torch.float32)
+
+    @property
+    def err_flags(self):
+        return self._view(self.c.err_flags, 1, torch.int32)
+
+    def read_counts(self) -> Tuple[np.ndarray, np.ndarray, int]:
+        """cnt, pad and the row total on the host (synchronises the stream)."""
+        E = self.cfg.num_experts
+        cnt = np.zeros(E, np.int32)
+        pad = np.zeros(E, np.int32)
+        rows = np.zeros(1, np.int64)
+        F.ep_handle_read_counts(self.c, cnt.ctypes.data, pad.ctypes.data, rows.ctypes.data, _stream())
+        return cnt, pad, int(rows[0])
+
+    def check(self) -> int:
+        """EP_ERRFLAG_* bits of the layout (synchronises the stream)."""
+        return F.ep_handle_check(self.c, _stream())
+
+
+def new_workspace(cfg: Config, device="cuda") -> torch.Tensor:
+    return torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def layout(cfg: Config, topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> Handle:
+    idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
+    T = int(topk_idx.shape[0])
+    if topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+        raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
+    if topk_w is not None and tuple(topk_w.shape) != tuple(topk_idx.shape):
+        raise ValueError("topk_w must match topk_idx")
+    if workspace is None:
+        workspace = new_workspace(cfg, topk_idx.device)
+    h = F.ep_layout(cfg.c(), T, _dev(topk_idx, "topk_idx", idx_dtype), _opt(topk_w, "topk_w", torch.float32),
+                    _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+    return Handle(cfg, h, workspace)
+
+
+def _recv_buffers(h: Handle, dtype: int, device, recv, recv_scales):
+    R, H = h.cfg.recv_rows_bound(), h.cfg.hidden
+    fp8 = dtype != BF16
+    if recv is None:
+        recv = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=device)
+    return recv, recv_scales
+
+
+def dispatch(h: Handle, x: torch.Tensor, dtype: int = BF16, x_scales: Optional[torch.Tensor] = None,
+             recv: Optional[torch.Tensor] = None, recv_scales: Optional[torch.Tensor] = None):
+    """Returns recv (and recv_scales for the FP8 types)."""
+    T, H, R = h.num_tokens, h.cfg.hidden, h.cfg.recv_rows_bound()
+    _need(x, (T, H), "x")
+    if dtype == FP8_PREQUANT:
+        _need(x_scales, (T, H // 128), "x_scales")
+    xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
+    recv, recv_scales = _recv_buffers(h, dtype, x.device, recv, recv_scales)
+    _need(recv, (R, H), "recv")
+    if dtype != BF16:
+        _need(recv_scales, (R, H // 128), "recv_scales")
+    F.ep_dispatch(h.c, dtype, _dev(x, "x", xdt), _opt(x_scales, "x_scales", torch.float32),
+                  _dev(recv, "recv", torch.uint8 if dtype != BF16 else torch.bfloat16),
+                  _opt(recv_scales, "recv_scales", torch.float32),
+                  _stream())
+    return (recv, recv_scales) if dtype != BF16 else recv
+
+
+def combine(h: Handle, y: torch.Tensor, topk_w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            row_vals: Optional[torch.Tensor] = None):
+    """Returns out [T, H] bf16 (and out_vals [T, k] when row_vals is given)."""
+    T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
+    _need(y, (h.cfg.recv_rows_bound(), H), "y")
+    _need(topk_w, (T, k), "topk_w")
+    _need(row_vals, (h.cfg.recv_rows_bound(),), "row_vals")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, (T, H), "out")
+    out_vals = None if row_vals is None else torch.empty((T, k), dtype=torch.float32, device=y.device)
+    F.ep_combine(h.c, _dev(y, "y", torch.bfloat16), _opt(topk_w, "topk_w", torch.float32),
+                 _dev(out, "out", torch.bfloat16), _opt(row_vals, "row_vals", torch.float32),
+                 _opt(out_vals, "out_vals", torch.float32), _stream())
+    return out if row_vals is None else (out, out_vals)
+
+
+def dispatch_backward(h: Handle, grad_recv: torch.Tensor, grad_row_w: Optional[torch.Tensor] = None):
+    """README dispatch_backward: returns grad_x (and grad_topk_w)."""
+    T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
+    _need(grad_recv, (h.cfg.recv_rows_bound(), H), "grad_recv")
+    _need(grad_row_w, (h.cfg.recv_rows_bound(),), "grad_row_w")
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
+    gw = None if grad_row_w is None else torch.empty((T, k), dtype=torch.float32, device=grad_recv.device)
+    F.ep_dispatch_backward(h.c, _dev(grad_recv, "grad_recv", torch.bfloat16),
+                           _opt(grad_row_w, "grad_row_w", torch.float32), _dev(gx, "grad_x", torch.bfloat16),
+                           _opt(gw, "grad_topk_w", torch.float32), _stream())
+    return gx if gw is None else (gx, gw)
+
+
+def combine_backward(h: Handle, grad_out: torch.Tensor, dtype: int = BF16, topk_w: Optional[torch.Tensor] = None,
+                     grad_y: Optional[torch.Tensor] = None, grad_y_scales: Optional[torch.Tensor] = None):
+    """README combine_backward: a dispatch of grad_out on the handle."""
+    T, H, R = h.num_tokens, h.cfg.hidden, h.cfg.recv_rows_bound()
+    _need(grad_out, (T, H), "grad_out")
+    _need(topk_w, (T, h.cfg.num_topk), "topk_w")
+    grad_y, grad_y_scales = _recv_buffers(h, dtype, grad_out.device, grad_y, grad_y_scales)
+    _need(grad_y, (R, H), "grad_y")
+    if dtype != BF16:
+        _need(grad_y_scales, (R, H // 128), "grad_y_scales")
+    F.ep_combine_backward(h.c, dtype, _dev(grad_out, "grad_out", torch.bfloat16),
+                          _opt(topk_w, "topk_w", torch.float32), _dev(grad_y, "grad_y", torch.uint8 if dtype != BF16 else torch.bfloat16),
+                          _opt(grad_y_scales, "grad_y_scales", torch.float32), _stream())
+    return (grad_y, grad_y_scales) if dtype != BF16 else grad_y

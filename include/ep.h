@@ -1,0 +1,234 @@
+/*
+ * ep.h — MoE dispatch / combine on one MI355X (gfx950): the C ABI.
+ *
+ * The operations follow the DeepEP README (community translation),
+ * section "Interfaces and examples":
+ *   - dispatch (README "Example use in model training or inference
+ *     prefilling", dispatch_forward): route each token's hidden row to the
+ *     experts of its top-k choice, into expert-contiguous receive rows whose
+ *     per-expert counts are padded to expert_alignment for the grouped GEMM;
+ *     x may be BF16 or FP8 with per-token scale factors;
+ *   - combine (combine_forward): reduce each token's k expert outputs back
+ *     into one BF16 row;
+ *   - dispatch_backward is a combine (also returning the combined weight
+ *     gradients); combine_backward is a dispatch that reuses the handle;
+ *   - handle caching for decode (README "Example use in inference decoding"):
+ *     a handle is reused across calls and skips the layout and the CPU sync.
+ * This library computes one GPU's share of that work: every receive row
+ * lives in this GPU's memory; there is no transport.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers (or host pointers the
+ *     device can access); "host" pointers are ordinary host memory.
+ *   - The caller owns every buffer: inputs, outputs and the workspace. The
+ *     library allocates no device memory, keeps no pointer after returning
+ *     and holds no global state except a thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the null stream). All work is
+ *     enqueued on it and runs asynchronously; only ep_handle_read_counts and
+ *     ep_handle_check wait for the stream.
+ *   - Argument errors (NULL or misaligned pointer, sizes out of range,
+ *     workspace too small) return EP_ERR_INVALID_ARG / EP_ERR_WORKSPACE /
+ *     EP_ERR_UNSUPPORTED immediately and enqueue nothing;
+ *     ep_last_error_message() says what was wrong. A failed launch returns
+ *     EP_ERR_HIP.
+ *   - Data errors found on the device (an expert id outside [0, E) that is
+ *     not -1; a fixed-capacity overflow) do not fail the call: the pair is
+ *     skipped (its slot is -1, it is copied nowhere and contributes nothing
+ *     to combine) and a sticky bit is set in the handle's error word, read
+ *     with ep_handle_check.
+ *   - Alignment: x, recv, y, out and their FP8 counterparts must be 16-byte
+ *     aligned; hidden must be a multiple of 8 (BF16) or 128 (FP8).
+ *   - Numbers: bf16 = bfloat16 bit patterns (uint16); FP8 = OCP E4M3FN bytes;
+ *     scales and weights are IEEE binary32.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,
+    EP_ERR_UNSUPPORTED = 2,
+    EP_ERR_HIP = 3,
+    EP_ERR_WORKSPACE = 4
+} ep_status;
+
+/* Receive layout.
+ * EP_MODE_COMPACT: expert-major rows, expert e owns
+ *   [expert_off[e], expert_off[e] + pad[e]) with pad[e] = ceil(cnt[e]/A)*A;
+ *   its first cnt[e] rows hold the pairs routed to e, the rest are padding.
+ * EP_MODE_FIXED: expert e owns [e*C, e*C + C) (a [E, C, hidden] buffer, the
+ *   decode layout); its first min(cnt[e], C) rows are written, the others
+ *   are left untouched. */
+typedef enum { EP_MODE_COMPACT = 0, EP_MODE_FIXED = 1 } ep_mode;
+
+/* Payload type of a dispatch.
+ * EP_BF16: x is bf16 [T, hidden]; recv is bf16 [rows, hidden].
+ * EP_FP8_QUANTIZE: x is bf16 [T, hidden]; each 1x128 block of a token is
+ *   quantised once (amax = max |x|, scale = amax / 448, code =
+ *   E4M3FN(x / scale) rounded to nearest even and saturated to +-448; an
+ *   all-zero block has scale 0 and zero codes); recv is E4M3FN
+ *   [rows, hidden], recv_scales is binary32 [rows, hidden/128] row-major.
+ * EP_FP8_PREQUANT: x is already E4M3FN [T, hidden] with x_scales binary32
+ *   [T, hidden/128] (the README's (data, scale_factors) tuple); codes and
+ *   scales are copied bitwise. */
+typedef enum { EP_BF16 = 0, EP_FP8_QUANTIZE = 1, EP_FP8_PREQUANT = 2 } ep_dtype;
+
+/* ep_config.flags */
+#define EP_FLAG_NO_ZERO_PAD 1u /* COMPACT: leave padding rows unwritten */
+
+/* Bits of the device error word (ep_handle_check). */
+#define EP_ERRFLAG_BAD_ID 1u   /* an id outside [0, E) other than -1 */
+#define EP_ERRFLAG_OVERFLOW 2u /* FIXED: more than C pairs for an expert */
+
+/* Static sizes of one layout; the README's buffer arguments
+ * (num_max_tokens_per_rank, hidden, num_topk, expert_alignment).
+ * Limits: 1 <= num_experts <= 1024, 1 <= num_topk <= 32,
+ * num_experts % num_dests == 0, max_tokens * num_topk < 2^31,
+ * hidden >= 8 and hidden % 8 == 0 (hidden % 128 == 0 for FP8),
+ * expert_alignment >= 1 (must be 1 in FIXED mode), capacity >= 1 in FIXED
+ * mode, idx_bits 64 (int64 topk_idx, torch.topk's type) or 32. */
+typedef struct {
+    int32_t max_tokens;       /* T_max: tokens a layout may hold */
+    int32_t hidden;           /* H */
+    int32_t num_experts;      /* E */
+    int32_t num_topk;         /* k */
+    int32_t num_dests;        /* D: experts grouped in D contiguous ranges */
+    int32_t expert_alignment; /* A */
+    int32_t capacity;         /* C: rows per expert in FIXED mode */
+    int32_t mode;             /* ep_mode */
+    int32_t idx_bits;         /* 64 or 32 */
+    uint32_t flags;           /* EP_FLAG_* */
+} ep_config;
+
+/* Routing metadata shared by dispatch, combine and the duals (the README's
+ * EPHandle). Plain data: copying it is fine. Every pointer points into the
+ * caller's workspace (device memory) and is valid while the workspace
+ * lives and no other ep_layout writes into it. Contents after the layout
+ * has run on the stream:
+ *   cnt[E]         pairs routed to each expert (before any capacity limit)
+ *   pad[E]         rows of expert e in the receive buffer (COMPACT: padded
+ *                  count; FIXED: min(cnt, C)) — the GEMM row counts
+ *   expert_off[E+1] first row of each expert (COMPACT: exclusive scan of pad;
+ *                  FIXED: e*C); expert_off[E] is the row total R
+ *   dest_off[D+1]  first row of each destination: expert_off[d*E/D]
+ *   dest_tokens[D] distinct tokens with a routed pair into destination d
+ *   slot[T*k]      receive row of pair (t, j) or -1 when skipped; rows of
+ *                  one expert are in ascending (t, j) order
+ *   row_src[Rcap]  pair index t*k + j held by each row; -1 on padding rows
+ *                  (COMPACT); FIXED rows past pad[e] are not written
+ *   row_w[Rcap]    topk_w of the pair held by each row, 0 on padding rows;
+ *                  written only when ep_layout got topk_w
+ *   err_flags[1]   EP_ERRFLAG_* bits raised by this layout */
+typedef struct {
+    ep_config cfg;
+    int32_t num_tokens;
+    int32_t num_blocks; /* internal: layout partition of the pairs */
+    int32_t* cnt;
+    int32_t* pad;
+    int32_t* expert_off;
+    int32_t* dest_off;
+    int32_t* dest_tokens;
+    int32_t* slot;
+    int32_t* row_src;
+    float* row_w;
+    uint32_t* err_flags;
+    void* internal; /* workspace scratch for the layout kernels */
+} ep_handle;
+
+/* Bytes of workspace one layout needs (the README's get_buffer_size_hint).
+ * Returns 0 when the config is invalid (see ep_last_error_message). */
+size_t ep_workspace_bytes(const ep_config* cfg);
+
+/* Rows a receive buffer must have to hold any layout of this config without
+ * knowing the counts: max_tokens*k + E*(A-1) (COMPACT) or E*C (FIXED).
+ * Returns -1 when the config is invalid. */
+int64_t ep_recv_rows_bound(const ep_config* cfg);
+
+/* Builds the layout of `num_tokens` tokens (README dispatch_forward: the
+ * per-expert counts and padded offsets; the stable slot of every pair).
+ *   cfg        host; copied into *out.
+ *   num_tokens 0 <= num_tokens <= cfg->max_tokens.
+ *   topk_idx   device [num_tokens, k], int64 or int32 per cfg->idx_bits;
+ *              -1 masks a pair.
+ *   topk_w     device [num_tokens, k] binary32, or NULL (row_w not written).
+ *   workspace  device, >= ep_workspace_bytes(cfg) bytes, 256-byte aligned;
+ *              must not be in use by another in-flight layout.
+ *   out        host; receives the handle (valid once the stream reaches it).
+ * Enqueues one kernel for small layouts (num_tokens * k <= 4096 and
+ * E <= 512), three otherwise. Never synchronises. */
+ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
+                    const float* topk_w, void* workspace, size_t workspace_bytes,
+                    ep_handle* out, void* stream);
+
+/* Dispatch on an existing handle (README dispatch_forward, or dispatch with a
+ * cached handle: no layout work, no synchronisation).
+ *   x          device [T, hidden]: bf16 (EP_BF16, EP_FP8_QUANTIZE) or E4M3FN
+ *              (EP_FP8_PREQUANT).
+ *   x_scales   device [T, hidden/128] binary32 for EP_FP8_PREQUANT, else NULL.
+ *   recv       device [ep_recv_rows_bound, hidden] bf16 or E4M3FN. Row
+ *              slot[t, j] receives token t's row. COMPACT padding rows are
+ *              zero-filled unless EP_FLAG_NO_ZERO_PAD; rows at or past
+ *              expert_off[E] are not touched.
+ *   recv_scales device [rows bound, hidden/128] binary32 for the FP8 types
+ *              (padding rows get 0), else NULL. */
+ep_status ep_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales,
+                      void* recv, float* recv_scales, void* stream);
+
+/* Combine (README combine_forward): for every token t and channel c,
+ *   acc = +0; for j = 0..k-1 with slot[t, j] >= 0:
+ *       acc = fmaf(topk_w[t, j], float(y[slot[t, j], c]), acc)
+ *   (acc = acc + float(y[...]) when topk_w is NULL);
+ *   out[t, c] = bf16(acc), round to nearest even.
+ *   y          device bf16 [rows bound, hidden] (expert outputs, receive
+ *              layout).
+ *   topk_w     device [T, k] binary32 or NULL.
+ *   out        device bf16 [T, hidden].
+ *   row_vals   device [rows bound] binary32 or NULL; with out_vals given,
+ *              out_vals[t, j] = row_vals[slot[t, j]] (0 for skipped pairs).
+ *   out_vals   device [T, k] binary32 or NULL. */
+ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_w, void* out,
+                     const float* row_vals, float* out_vals, void* stream);
+
+/* README dispatch_backward: the backward of a dispatch is a combine without
+ * weights; grad_row_w (per receive row, e.g. the gradient of row_w) is
+ * gathered back to grad_topk_w [T, k] when both are given. */
+ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const float* grad_row_w,
+                               void* grad_x, float* grad_topk_w, void* stream);
+
+/* README combine_backward: the backward of a combine is a dispatch of the
+ * output gradient on the same handle. With topk_w (EP_BF16 only), the copy
+ * for pair (t, j) is bf16(topk_w[t, j] * float(grad_out[t, c])), the
+ * gradient of the weighted combine; EP_FP8_QUANTIZE with topk_w returns
+ * EP_ERR_UNSUPPORTED. */
+ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* grad_out,
+                              const float* topk_w, void* grad_y, float* grad_y_scales,
+                              void* stream);
+
+/* Copies cnt and pad (host arrays of E, either may be NULL) and the row
+ * total R (host, may be NULL) to the host. Synchronises the stream: this is
+ * the README's "CPU sync" of a non-cached dispatch. */
+ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, int64_t* rows,
+                                void* stream);
+
+/* Reads the handle's error word (EP_ERRFLAG_* bits) to host *flags.
+ * Synchronises the stream. */
+ep_status ep_handle_check(const ep_handle* h, uint32_t* flags, void* stream);
+
+/* Static text for a status code. */
+const char* ep_status_string(ep_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ep_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/ep.h declares, sizes workspaces and rejects bad arguments before
+touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_ep_layout_10_amd import _ffi as F
+from ep_workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "ep.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 11, names
+    lib = F.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in F._SIGNATURES, n
+
+
+def cfg(**kw):
+    base = dict(max_tokens=64, hidden=256, num_experts=16, num_topk=2, num_dests=1, expert_alignment=1,
+                capacity=0, mode=F.EP_MODE_COMPACT, idx_bits=64, flags=0)
+    base.update(kw)
+    return F.ep_config(**base)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_rows_bound_and_workspace(name):
+    wl = WORKLOADS[name]
+    c = cfg(max_tokens=wl.T, hidden=wl.H, num_experts=wl.E, num_topk=wl.k, num_dests=wl.D,
+            expert_alignment=wl.A, capacity=wl.C, mode=wl.mode)
+    assert F.ep_recv_rows_bound(c) == wl.recv_rows_bound
+    ws = F.ep_workspace_bytes(c)
+    # at least slot + row_src + row_w + counts
+    assert ws >= 4 * (wl.T * wl.k + 2 * wl.recv_rows_bound + 2 * wl.E)
+    assert ws % 256 == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_experts=0), dict(num_experts=1025), dict(num_topk=0), dict(num_topk=33),
+    dict(num_dests=3), dict(hidden=100), dict(hidden=0), dict(idx_bits=16),
+    dict(expert_alignment=0), dict(mode=2), dict(mode=F.EP_MODE_FIXED, capacity=0),
+    dict(mode=F.EP_MODE_FIXED, capacity=4, expert_alignment=2), dict(flags=8), dict(max_tokens=-1),
+    dict(max_tokens=1 << 30, num_topk=4),
+])
+def test_invalid_configs(bad):
+    c = cfg(**bad)
+    assert F.ep_workspace_bytes(c) == 0
+    assert F.ep_recv_rows_bound(c) == -1
+    assert F.last_error_message() != ""
+    h = F.ep_handle()
+    st = F.lib().ep_layout(ctypes.byref(c), 1, ctypes.c_void_p(256), None, ctypes.c_void_p(256), 1 << 30,
+                           ctypes.byref(h), None)
+    assert st == F.EP_ERR_INVALID_ARG
+
+
+def test_layout_argument_errors():
+    c = cfg()
+    lib = F.lib()
+    h = F.ep_handle()
+    need = F.ep_workspace_bytes(c)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks first
+    assert lib.ep_layout(None, 1, fake, None, fake, need, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_layout(ctypes.byref(c), 65, fake, None, fake, need, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_layout(ctypes.byref(c), -1, fake, None, fake, need, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_layout(ctypes.byref(c), 4, None, None, fake, need, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_layout(ctypes.byref(c), 4, fake, None, None, need, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_layout(ctypes.byref(c), 4, fake, None, ctypes.c_void_p((1 << 20) + 8), need,
+                         ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG     # misaligned workspace
+    assert lib.ep_layout(ctypes.byref(c), 4, fake, None, fake, need - 1, ctypes.byref(h), None) == F.EP_ERR_WORKSPACE
+    assert "needs" in F.last_error_message()
+    assert lib.ep_layout(ctypes.byref(c), 4, fake, None, fake, need, None, None) == F.EP_ERR_INVALID_ARG
+
+
+def fake_handle(**kw):
+    h = F.ep_handle()
+    h.cfg = cfg(**kw)
+    h.num_tokens = 4
+    for f in ("cnt", "pad", "expert_off", "dest_off", "dest_tokens", "slot", "row_src", "row_w", "err_flags"):
+        setattr(h, f, 1 << 20)
+    return h
+
+
+def test_dispatch_combine_argument_errors():
+    lib = F.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    h = fake_handle()
+    assert lib.ep_dispatch(None, F.EP_BF16, fake, None, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(h), 7, fake, None, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(h), F.EP_BF16, None, None, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(h), F.EP_BF16, ctypes.c_void_p((1 << 20) + 2), None, fake, None,
+                           None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(h), F.EP_FP8_QUANTIZE, fake, None, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(h), F.EP_FP8_PREQUANT, fake, None, fake, fake, None) == F.EP_ERR_INVALID_ARG
+    h2 = fake_handle(hidden=200)
+    assert lib.ep_dispatch(ctypes.byref(h2), F.EP_FP8_QUANTIZE, fake, None, fake, fake, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_combine(ctypes.byref(h), None, None, fake, None, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_combine(ctypes.byref(h), fake, None, fake, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_QUANTIZE, fake, fake, fake, fake,
+                                   None) == F.EP_ERR_UNSUPPORTED
+    h3 = fake_handle()
+    h3.num_tokens = 65
+    assert lib.ep_combine(ctypes.byref(h3), fake, None, fake, None, None, None) == F.EP_ERR_INVALID_ARG
+    h4 = fake_handle()
+    h4.slot = None
+    assert lib.ep_dispatch(ctypes.byref(h4), F.EP_BF16, fake, None, fake, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_handle_check(None, None, None) == F.EP_ERR_INVALID_ARG
+    assert lib.ep_handle_check(ctypes.byref(h), None, None) == F.EP_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s, n in ((0, "EP_OK"), (1, "EP_ERR_INVALID_ARG"), (2, "EP_ERR_UNSUPPORTED"), (3, "EP_ERR_HIP"),
+                 (4, "EP_ERR_WORKSPACE"), (99, "EP_ERR_UNKNOWN")):
+        assert F.status_string(s) == n
+
+
+def test_struct_sizes_match_header():
+    # ep_config: 10 x 4 bytes; ep_handle: config + 2 ints + 10 pointers
+    assert ctypes.sizeof(F.ep_config) == 40
+    assert ctypes.sizeof(F.ep_handle) == 40 + 8 + 10 * 8

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: layout, slots, copies, FP8 codes and scales bit-exact; combine within
+1 bf16 ulp (bit-exact expected: both sides sum in binary32 with fused
+multiply-add in k order). All five workloads run at their full sizes, in the
+launch configuration the benchmark uses."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ep_workloads import WORKLOADS, make_inputs, random_routing_table, f32_to_bf16_bits
+from gpu_common import (log, to_dev, to_dev_bf16, bf16_host, host, cfg_of, workload_case, written_rows,
+                        bf16_ulp_distance, compare_layout)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from combine_ep_layout_10_amd import ops
+
+
+def _run_small(T, H, E, k, A=1, D=1, C=0, mode=0, seed=0, masked=0.0, bad=0.0, distinct=True,
+               idx_bits=64, flags=0, dispatch="bf16", weights=True):
+    """Random small case through every stage, checked against the oracle."""
+    log("case T=%d H=%d E=%d k=%d A=%d D=%d C=%d mode=%d idx_bits=%d dispatch=%s seed=%d"
+        % (T, H, E, k, A, D, C, mode, idx_bits, dispatch, seed))
+    rng = np.random.default_rng(seed)
+    idx = random_routing_table(rng, T, E, k, masked_frac=masked, bad_frac=bad, distinct=distinct)
+    if idx_bits == 32:
+        idx = idx.astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32) if weights else None
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lay = oracle.layout(mode, T, E, k, A, D, C, idx, w)
+    cfg = ops.Config(max_tokens=max(T, 1), hidden=H, num_experts=E, num_topk=k, num_dests=D,
+                     expert_alignment=A, capacity=C, mode=mode, idx_bits=idx_bits, flags=flags)
+    h = ops.layout(cfg, to_dev(idx), None if w is None else to_dev(w))
+    compare_layout(h, lay, weights=w is not None)
+    R = cfg.recv_rows_bound()
+    rows = written_rows(lay)
+    zero_pad = not (flags & ops.FLAG_NO_ZERO_PAD)
+    if mode == oracle.MODE_COMPACT and not zero_pad:
+        rows = rows[lay["row_src"][rows] >= 0]
+    if dispatch == "bf16":
+        ref = oracle.dispatch_bf16(lay, x, k, zero_pad=zero_pad)
+        recv = torch.full((R, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        ops.dispatch(h, to_dev_bf16(x), ops.BF16, recv=recv)
+        got = bf16_host(recv)
+        assert np.array_equal(got[rows], ref[rows])
+        untouched = np.setdiff1d(np.arange(R), rows)
+        assert np.all(got[untouched] == 0xFFFF)
+    else:
+        q, s = oracle.dispatch_fp8(lay, x, k, zero_pad=zero_pad)
+        recv = torch.full((R, H), 0xEE, dtype=torch.uint8, device="cuda")
+        rs = torch.full((R, H // 128), -7.0, dtype=torch.float32, device="cuda")
+        ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE, recv=recv, recv_scales=rs)
+        assert np.array_equal(host(recv)[rows], q[rows])
+        assert np.array_equal(host(rs)[rows].view(np.uint32), s[rows].view(np.uint32))
+        untouched = np.setdiff1d(np.arange(R), rows)
+        assert np.all(host(recv)[untouched] == 0xEE)
+    # combine over random expert outputs
+    y = f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    out_ref, vals_ref = oracle.combine(lay, y, k, w, row_vals=lay["row_w"] if w is not None else None)
+    res = ops.combine(h, to_dev_bf16(y), None if w is None else to_dev(w),
+                      row_vals=h.row_w if w is not None else None)
+    out = res[0] if w is not None else res
+    got = bf16_host(out)
+    assert bf16_ulp_distance(got, out_ref).max(initial=0) <= 1
+    assert np.array_equal(got, out_ref), "combine differs from the oracle (within 1 ulp)"
+    if w is not None:
+        assert np.array_equal(host(res[1]).view(np.uint32), vals_ref.view(np.uint32))
+    return h, lay
+
+
+# ---------------------------------------------------------------- small cases
+
+def test_tiny_hand_example():
+    _run_small(3, 256, 4, 2, A=2, D=2, seed=1)
+
+
+@pytest.mark.parametrize("T,E,k,A,D", [
+    (1, 16, 2, 1, 1), (37, 8, 3, 4, 2), (128, 16, 2, 1, 1), (300, 24, 5, 7, 3),
+    (819, 64, 5, 128, 4),        # P = 4095: single-block path
+    (820, 64, 5, 128, 4),        # P = 4100: multi-block path
+    (2049, 600, 2, 8, 6),        # E > 512: multi-block path with few pairs
+    (5000, 1024, 7, 3, 32),      # largest E
+])
+def test_random_layouts(T, E, k, A, D):
+    _run_small(T, 64, E, k, A=A, D=D, seed=T + E)
+
+
+def test_masked_and_bad_ids():
+    h, lay = _run_small(500, 128, 12, 4, A=3, D=4, seed=3, masked=0.2, bad=0.05, distinct=False)
+    assert lay["flags"] == oracle.FLAG_BAD_ID and h.check() == oracle.FLAG_BAD_ID
+    h, lay = _run_small(6000, 64, 40, 3, A=16, D=2, seed=4, masked=0.1, bad=0.01, distinct=False)
+    assert h.check() == oracle.FLAG_BAD_ID
+
+
+def test_int32_indices_and_fp8():
+    _run_small(700, 256, 32, 4, A=32, D=4, seed=5, idx_bits=32, dispatch="fp8")
+    _run_small(3000, 384, 96, 6, A=64, D=8, seed=6, idx_bits=32, dispatch="fp8")
+
+
+def test_fixed_capacity_and_overflow():
+    h, lay = _run_small(128, 256, 16, 4, mode=1, C=64, seed=7, dispatch="fp8")
+    assert h.check() == 0
+    h, lay = _run_small(200, 128, 8, 3, mode=1, C=20, seed=8)       # overflow
+    assert lay["flags"] == oracle.FLAG_OVERFLOW and h.check() == oracle.FLAG_OVERFLOW
+    h, lay = _run_small(3000, 128, 8, 3, mode=1, C=500, seed=9)     # multi-block, overflow
+    assert h.check() == oracle.FLAG_OVERFLOW
+
+
+def test_no_zero_pad_flag():
+    _run_small(333, 128, 16, 3, A=16, D=2, seed=10, flags=ops.FLAG_NO_ZERO_PAD)
+    _run_small(333, 256, 16, 3, A=16, D=2, seed=11, flags=ops.FLAG_NO_ZERO_PAD, dispatch="fp8")
+
+
+def test_unweighted_and_k1():
+    _run_small(99, 64, 5, 1, A=4, seed=12)
+    _run_small(99, 64, 5, 3, A=4, seed=13, weights=False)
+
+
+def test_empty_batch():
+    cfg = ops.Config(max_tokens=16, hidden=128, num_experts=8, num_topk=2, expert_alignment=4)
+    idx = torch.zeros((0, 2), dtype=torch.int64, device="cuda")
+    h = ops.layout(cfg, idx)
+    cnt, pad, R = h.read_counts()
+    assert R == 0 and cnt.sum() == 0 and h.check() == 0
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    ops.dispatch(h, x)
+    y = torch.zeros((cfg.recv_rows_bound(), 128), dtype=torch.bfloat16, device="cuda")
+    out = ops.combine(h, y)
+    assert out.shape == (0, 128)
+    torch.cuda.synchronize()
+
+
+def test_argument_errors_enqueue_nothing():
+    cfg = ops.Config(max_tokens=4, hidden=100, num_experts=8, num_topk=2)
+    with pytest.raises(Exception):
+        ops.new_workspace(cfg)
+    cfg = ops.Config(max_tokens=4, hidden=128, num_experts=8, num_topk=2)
+    idx = torch.zeros((5, 2), dtype=torch.int64, device="cuda")
+    with pytest.raises(Exception):
+        ops.layout(cfg, idx)                                # T > max_tokens
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Exception):
+        ops.layout(cfg, idx[:4], workspace=ws)              # workspace too small
+
+
+# ---------------------------------------------------------------- duals
+
+def test_backward_duals():
+    rng = np.random.default_rng(14)
+    T, H, E, k, A = 400, 256, 16, 4, 8
+    idx = random_routing_table(rng, T, E, k, masked_frac=0.05)
+    w = rng.random((T, k)).astype(np.float32)
+    lay = oracle.layout(0, T, E, k, A, 1, 0, idx, w)
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A)
+    h = ops.layout(cfg, to_dev(idx), to_dev(w))
+    R = cfg.recv_rows_bound()
+    # dispatch_backward = unweighted combine + gather of row grads
+    g = f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    grow = rng.standard_normal(R).astype(np.float32)
+    ref_x, ref_w = oracle.dispatch_backward(lay, g, k, grow)
+    gx, gw = ops.dispatch_backward(h, to_dev_bf16(g), to_dev(grow))
+    assert np.array_equal(bf16_host(gx), ref_x)
+    assert np.array_equal(host(gw).view(np.uint32), ref_w.view(np.uint32))
+    # combine_backward = dispatch of grad_out, weighted per pair (BF16)
+    go = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ref = oracle.combine_backward_bf16(lay, go, k, w)
+    gy = ops.combine_backward(h, to_dev_bf16(go), ops.BF16, to_dev(w))
+    rows = np.arange(lay["rows"])
+    assert np.array_equal(bf16_host(gy)[rows], ref[rows])
+    # unweighted and FP8 combine_backward
+    ref = oracle.combine_backward_bf16(lay, go, k, None)
+    gy = ops.combine_backward(h, to_dev_bf16(go), ops.BF16)
+    assert np.array_equal(bf16_host(gy)[rows], ref[rows])
+    q, s = oracle.dispatch_fp8(lay, go, k)
+    gq, gs = ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE)
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
+    with pytest.raises(Exception):
+        ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE, to_dev(w))
+
+
+def test_fp8_prequant_passthrough():
+    rng = np.random.default_rng(15)
+    T, H, E, k, A = 300, 512, 16, 4, 16
+    idx = random_routing_table(rng, T, E, k)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lay = oracle.layout(0, T, E, k, A, 1, 0, idx)
+    xq = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    q, s = oracle.dispatch_fp8_prequant(lay, xq, xs, k)
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A)
+    h = ops.layout(cfg, to_dev(idx))
+    gq, gs = ops.dispatch(h, to_dev(xq), ops.FP8_PREQUANT, x_scales=to_dev(xs))
+    rows = np.arange(lay["rows"])
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
+
+
+def test_identity_round_trip_gpu():
+    """dispatch -> identity experts -> combine with softmax weights == x."""
+    wl = WORKLOADS["mid"]
+    inp = make_inputs(wl, with_y=False)
+    cfg = cfg_of(wl)
+    h = ops.layout(cfg, to_dev(inp["topk_idx"]), to_dev(inp["topk_w"]))
+    recv = ops.dispatch(h, to_dev_bf16(inp["x"]))
+    out = ops.combine(h, recv, to_dev(inp["topk_w"]))
+    ref = np.where(inp["x"] == 0x8000, 0, inp["x"])
+    assert np.array_equal(bf16_host(out), ref)
+
+
+# ---------------------------------------------------------------- FP8 codec
+
+def test_fp8_codec_all_bf16_patterns():
+    """Every finite bf16 pattern is quantised on the GPU under a grid of block
+    scales, bit-exact against the oracle. Values are sorted by magnitude
+    and packed 127 per 128-block with one element setting the block's amax
+    to (largest value in the block) * factor."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    vals = bits[np.isfinite(v)].astype(np.uint16)
+    mag = np.abs((vals.astype(np.uint32) << 16).view(np.float32))
+    vals = vals[np.argsort(mag, kind="stable")]
+    nblk = -(-vals.size // 127)
+    padded = np.zeros(nblk * 127, np.uint16)
+    padded[:vals.size] = vals
+    blocks = padded.reshape(nblk, 127)
+    bm = np.abs((blocks.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
+    for factor in (1.0, 1.5, 3.0, 2.0 ** 9, 2.0 ** 20):
+        top = float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])   # largest finite bf16
+        amax = f32_to_bf16_bits(np.minimum(np.maximum(bm, 2.0 ** -100) * factor, top).astype(np.float32))
+        x = np.concatenate([amax[:, None], blocks], axis=1)            # [nblk, 128]
+        T = nblk
+        H = 128
+        idx = np.zeros((T, 1), np.int64)
+        lay = oracle.layout(0, T, 1, 1, 1, 1, 0, idx)
+        q, s = oracle.dispatch_fp8(lay, x, 1)
+        cfg = ops.Config(max_tokens=T, hidden=H, num_experts=1, num_topk=1)
+        h = ops.layout(cfg, to_dev(idx))
+        gq, gs = ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE)
+        assert np.array_equal(host(gq)[:T], q[:T]), factor
+        assert np.array_equal(host(gs)[:T].view(np.uint32), s[:T].view(np.uint32)), factor
+
+
+# ---------------------------------------------------------------- determinism
+
+def test_repeat_is_bit_identical():
+    wl = WORKLOADS["skewed_v3"].with_tokens(2048)
+    inp = make_inputs(wl, with_y=False)
+    cfg = cfg_of(wl)
+    outs = []
+    for _ in range(2):
+        h = ops.layout(cfg, to_dev(inp["topk_idx"]), to_dev(inp["topk_w"]))
+        q, s = ops.dispatch(h, to_dev_bf16(inp["x"]), ops.FP8_QUANTIZE)
+        torch.cuda.synchronize()
+        outs.append((host(h.slot).copy(), host(q).copy(), host(s).copy()))
+    R = int(host(h.expert_off)[-1])
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1][:R], outs[1][1][:R])
+    assert np.array_equal(outs[0][2][:R], outs[1][2][:R])
+
+
+# ---------------------------------------------------------------- full workloads
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3", "skewed_v3"])
+def test_workload_full_size(name):
+    """Every workload at its full size: layout, dispatch and combine."""
+    log("workload %s: preparing inputs and oracle" % name)
+    case = workload_case(name)
+    wl, inp, lay = case["wl"], case["inp"], case["lay"]
+    log("workload %s: GPU run" % name)
+    cfg = cfg_of(wl)
+    h = ops.layout(cfg, to_dev(inp["topk_idx"]), to_dev(inp["topk_w"]))
+    compare_layout(h, lay)
+    rows = written_rows(lay)
+    x = to_dev_bf16(inp["x"])
+    if wl.dispatch == "fp8":
+        R = cfg.recv_rows_bound()
+        recv = torch.full((R, wl.H), 0xEE, dtype=torch.uint8, device="cuda")
+        rs = torch.full((R, wl.H // 128), -7.0, dtype=torch.float32, device="cuda")
+        ops.dispatch(h, x, ops.FP8_QUANTIZE, recv=recv, recv_scales=rs)
+        assert np.array_equal(host(recv)[rows], case["recv"][rows])
+        assert np.array_equal(host(rs)[rows].view(np.uint32), case["recv_scales"][rows].view(np.uint32))
+        if wl.mode == oracle.MODE_FIXED:
+            untouched = np.setdiff1d(np.arange(R), rows)
+            assert np.all(host(recv)[untouched] == 0xEE)
+        del recv, rs
+    else:
+        recv = ops.dispatch(h, x)
+        assert np.array_equal(bf16_host(recv)[rows], case["recv"][rows])
+        del recv
+    y = to_dev_bf16(inp["y"])
+    out, vals = ops.combine(h, y, to_dev(inp["topk_w"]), row_vals=h.row_w)
+    got = bf16_host(out)
+    d = bf16_ulp_distance(got, case["out"])
+    log("workload %s: combine max ulp %d, differing %d" % (name, d.max(), int((d > 0).sum())))
+    assert d.max() <= 1
+    assert np.array_equal(host(vals).view(np.uint32), case["out_vals"].view(np.uint32))
+    del y, out, x
+    torch.cuda.empty_cache()
