@@ -39,7 +39,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
             for (int u = 0; u < 8; ++u) {
                 s[u] = j0 + u < a.k ? __builtin_amdgcn_readlane(my_s, j0 + u) : -1;
                 v[u] = make_uint4(0u, 0u, 0u, 0u);
-                if (s[u] >= 0) v[u] = ((const uint4*)(a.y + (int64_t)s[u] * a.H))[c];
+                if (s[u] >= 0) v[u] = load_stream((const uint4*)(a.y + (int64_t)s[u] * a.H) + c);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
         o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
         o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-        ((uint4*)(a.out + (int64_t)t * a.H))[c] = o;
+        store_stream((uint4*)(a.out + (int64_t)t * a.H) + c, o);
     }
 }
 

@@ -41,6 +41,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
     return sign | code;
 }
 
+// ---------------------------------------------------------------- memory
+
+// Streaming (non-temporal) 16-byte accesses for data touched once: on gfx950
+// they keep single-use rows from displacing reusable lines in L2 and MALL and
+// raise the sustained write rate well above plain stores.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, (u32x4_t*)p);
+}
+
+__device__ __forceinline__ void store_stream_f32(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 // ---------------------------------------------------------------- wave ops
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

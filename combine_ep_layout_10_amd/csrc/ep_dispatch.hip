@@ -11,6 +11,10 @@
 // lanes with DPP, and the lane writes its 16 E4M3 codes as one dwordx4.
 // Padding rows of the aligned layout are cleared by extra blocks placed
 // first in the grid, so they overlap with the token blocks.
+// Cache policy (measured on MI355X at the 8K x 7168 x top-8 shape): the k
+// payload rows go out with streaming stores; x is read with plain loads and
+// the 32-byte pieces of each scale row with plain stores, which L2 merges
+// into whole lines (streaming either of them cost about 30 us per call).
 #include "ep_internal.h"
 
 namespace ep {
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
         for (int r = r0; r < r1; ++r) {
             uint4* dst = (uint4*)((char*)a.recv + (int64_t)r * row_out);
-            for (int c = tid; c < nvec; c += nthreads) dst[c] = z;
+            for (int c = tid; c < nvec; c += nthreads) store_stream(dst + c, z);
             if (kFp8)
                 for (int b = tid; b < nb; b += nthreads) a.recv_scales[(int64_t)r * nb + b] = 0.0f;
         }
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
                     for (int i = 0; i < 8; ++i) g[i] = wj * f[i];
                     o = pack_bf16x8(g);
                 }
-                ((uint4*)((char*)a.recv + (int64_t)s * row_out))[c] = o;
+                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
             }
         }
     } else if (KIND == kDispatchFp8Quant) {
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
                 for (int j = 0; j < a.k; ++j) {
                     const int s = __builtin_amdgcn_readlane(my_s, j);
                     if (s < 0) continue;
-                    ((uint4*)((char*)a.recv + (int64_t)s * row_out))[c] = o;
+                    store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
                     if ((c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = scale;
                 }
             }
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
             for (int j = 0; j < a.k; ++j) {
                 const int s = __builtin_amdgcn_readlane(my_s, j);
                 if (s < 0) continue;
-                ((uint4*)((char*)a.recv + (int64_t)s * row_out))[c] = v;
+                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, v);
                 if (scale_lane) a.recv_scales[(int64_t)s * nb + (c >> 3)] = sc;
             }
         }

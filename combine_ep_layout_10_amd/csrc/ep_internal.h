@@ -9,10 +9,9 @@
 
 namespace ep {
 
-// Multi-block layout: waves per block and groups of 64 pairs per wave.
-constexpr int kLayoutWaves = 4;
-constexpr int kLayoutIters = 8;
-constexpr int kLayoutPairsPerBlock = kLayoutWaves * kLayoutIters * kWave;  // 2048
+// Multi-block layout: waves per block, one group of 64 pairs per wave.
+constexpr int kLayoutWaves = 16;
+constexpr int kLayoutPairsPerBlock = kLayoutWaves * kWave;  // 1024
 // Single-block layout limits.
 constexpr int kSmallMaxPairs = 4096;
 constexpr int kSmallMaxExperts = 512;

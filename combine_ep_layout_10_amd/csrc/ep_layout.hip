@@ -27,6 +27,36 @@ __device__ __forceinline__ int load_id(const LayoutArgs& a, int64_t p, bool& val
     return valid ? (int)v : 0;
 }
 
+// Loads the id of this lane's pair in the group at `base`.
+__device__ __forceinline__ int load_group(const LayoutArgs& a, int64_t base, bool& v, bool& bad) {
+    const int64_t p = base + lane_id();
+    v = false;
+    bad = false;
+    return p < (int64_t)a.T * a.k ? load_id(a, p, v, bad) : 0;
+}
+
+// Pair (t, j) is counted for destination dd when no earlier pair of token t
+// goes to dd. Earlier pairs in this group of 64 are read from their lanes;
+// those in an earlier group are loaded.
+__device__ __forceinline__ bool first_in_dest(const LayoutArgs& a, int64_t base, int dd, bool v) {
+    const int lane = lane_id();
+    const int64_t p = base + lane;
+    const int j = (int)(p % a.k);
+    bool first = v;
+    for (int m = 1; m < a.k; ++m) {
+        const int other = __shfl(dd, (lane - m) & (kWave - 1), kWave);
+        if (m <= j && lane >= m && other == dd) first = false;
+    }
+    if (v && j > lane) {
+        for (int jj = 0; jj < j - lane; ++jj) {
+            bool v2, b2;
+            const int e2 = load_id(a, p - j + jj, v2, b2);
+            if (v2 && e2 / a.epd == dd) first = false;
+        }
+    }
+    return first;
+}
+
 // One wave ranks its chunk [base, base + IT*64) in order. On return:
 //   ids/val hold each lane's expert per group; rank[it] = rank of the pair
 //   inside this wave's chunk among pairs of the same expert;
@@ -56,99 +86,108 @@ __device__ __forceinline__ bool wave_rank(const LayoutArgs& a, int64_t base, int
         rank[it] = pre + __popcll(peers & lanes_below(lane));
         if (v && (int)(__ffsll((long long)peers) - 1) == lane) wcnt[e] = pre + __popcll(peers);
         if (DEST) {
-            // Distinct tokens per destination: count pair (t, j) when no
-            // earlier pair (t, j') of its token is routed into the same
-            // destination. Earlier pairs in this group of 64 are read from
-            // their lanes; those in an earlier group are loaded.
-            const int64_t p = base + it * kWave + lane;
-            const int j = (int)(p % a.k);
             const int dd = v ? e / a.epd : -1;
-            bool first = v;
-            for (int m = 1; m < a.k; ++m) {
-                const int other = __shfl(dd, (lane - m) & (kWave - 1), kWave);
-                if (m <= j && lane >= m && other == dd) first = false;
-            }
-            if (v && j > lane) {
-                for (int jj = 0; jj < j - lane; ++jj) {
-                    bool v2, b2;
-                    const int e2 = load_id(a, p - j + jj, v2, b2);
-                    if (v2 && e2 / a.epd == dd) first = false;
-                }
-            }
-            if (first) atomicAdd(&dh[dd], 1);
+            if (first_in_dest(a, base + it * kWave, dd, v)) atomicAdd(&dh[dd], 1);
         }
     }
     return bad_any;
 }
 
 // ---------------------------------------------------------------- multi-block
+// A block is kLayoutWaves waves; each wave owns one group of 64 consecutive
+// pairs, so a block covers kLayoutPairsPerBlock consecutive pairs.
 
-template <int NW, int IT>
-__global__ __launch_bounds__(NW * 64) void k_layout_count(LayoutArgs a) {
+// Per-block expert counts, distinct-token counts per destination, bad ids.
+__global__ __launch_bounds__(kLayoutWaves * 64) void k_layout_count(LayoutArgs a) {
     extern __shared__ int32_t lds[];
-    int32_t* wcnt = lds;               // [NW][E]
-    int32_t* dh = lds + NW * a.E;      // [D]
-    const int tid = threadIdx.x, w = tid >> 6;
-    for (int i = tid; i < NW * a.E + a.D; i += NW * 64) lds[i] = 0;
+    int32_t* hist = lds;          // [E]
+    int32_t* dh = lds + a.E;      // [D]
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < a.E + a.D; i += blockDim.x) lds[i] = 0;
+    const int64_t base = ((int64_t)blockIdx.x * kLayoutWaves + w) * kWave;
+    bool v, bad;
+    const int e = load_group(a, base, v, bad);
+    const uint64_t peers = match_peers(e, v, a.nbits);
+    const int dd = v ? e / a.epd : -1;
+    const bool first = first_in_dest(a, base, dd, v);
     __syncthreads();
-    const int64_t base = ((int64_t)blockIdx.x * NW + w) * (IT * kWave);
-    int ids[IT], rank[IT];
-    bool val[IT];
-    bool bad = wave_rank<IT, true>(a, base, ids, val, rank, wcnt + w * a.E, dh);
+    if (v && (int)(__ffsll((long long)peers) - 1) == lane) atomicAdd(&hist[e], __popcll(peers));
+    if (first) atomicAdd(&dh[dd], 1);
     bad = __syncthreads_or(bad);
-    for (int e = tid; e < a.E; e += NW * 64) {
-        int s = 0;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) s += wcnt[ww * a.E + e];
-        a.bpart[(int64_t)blockIdx.x * a.E + e] = s;
-    }
-    for (int d = tid; d < a.D; d += NW * 64) a.dpart[(int64_t)blockIdx.x * a.D + d] = dh[d];
+    for (int i = tid; i < a.E; i += blockDim.x) a.bpart[(int64_t)blockIdx.x * a.E + i] = hist[i];
+    for (int d = tid; d < a.D; d += blockDim.x) a.dpart[(int64_t)blockIdx.x * a.D + d] = dh[d];
     if (tid == 0) a.fpart[blockIdx.x] = bad ? EP_ERRFLAG_BAD_ID : 0u;
 }
 
-// Pads, offsets and per-block bases. One block of 1024 threads; E <= 1024.
-__global__ __launch_bounds__(1024) void k_layout_scan(LayoutArgs a) {
+// Counts, pads, offsets and the base of every block inside every expert.
+// One block of 1024 threads; E <= 1024. Each expert's prefix over the count
+// blocks is split between tpe threads (contiguous block ranges), so the
+// loads of one expert column are issued in parallel.
+__global__ __launch_bounds__(1024) void k_layout_scan(LayoutArgs a, int tpe) {
     __shared__ int32_t s_off[1025];
+    __shared__ int32_t s_part[1024];
+    __shared__ int32_t s_dest[1024];
     __shared__ int tmp[17];
     const int tid = threadIdx.x;
     uint32_t f = 0;
     for (int b = tid; b < a.nblk; b += 1024) f |= a.fpart[b];
-    int padv = 0;
-    if (tid < a.E) {
-        const int e = tid;
-        int run = 0;
-        for (int b0 = 0; b0 < a.nblk; b0 += 16) {
-            int v[16];
+    for (int d = tid; d < a.D; d += 1024) s_dest[d] = 0;
+    __syncthreads();
+    for (int i = tid; i < a.nblk * a.D; i += 1024) atomicAdd(&s_dest[i % a.D], a.dpart[i]);
+
+    const int e = tid / tpe, q = tid % tpe;
+    const bool col = e < a.E;
+    const int per = (a.nblk + tpe - 1) / tpe;
+    const int b0 = q * per, b1 = min(a.nblk, b0 + per);
+    int cache[16];
+    int sum = 0;
+    if (col) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = (b0 + u < a.nblk) ? a.bpart[(int64_t)(b0 + u) * a.E + e] : 0;
+        for (int u = 0; u < 16; ++u) cache[u] = (b0 + u < b1) ? a.bpart[(int64_t)(b0 + u) * a.E + e] : 0;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if (b0 + u < a.nblk) a.bpart[(int64_t)(b0 + u) * a.E + e] = run;
-                run += v[u];
-            }
+        for (int u = 0; u < 16; ++u) sum += cache[u];
+        for (int b = b0 + 16; b < b1; ++b) sum += a.bpart[(int64_t)b * a.E + e];
+    }
+    s_part[tid] = sum;
+    __syncthreads();
+    int pre = 0, total = 0;
+    if (col) {
+        for (int qq = 0; qq < tpe; ++qq) {
+            const int v = s_part[e * tpe + qq];
+            if (qq < q) pre += v;
+            total += v;
         }
-        a.cnt[e] = run;
+        int run = pre;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (b0 + u < b1) a.bpart[(int64_t)(b0 + u) * a.E + e] = run;
+            run += cache[u];
+        }
+        for (int b = b0 + 16; b < b1; ++b) {
+            const int v = a.bpart[(int64_t)b * a.E + e];
+            a.bpart[(int64_t)b * a.E + e] = run;
+            run += v;
+        }
+    }
+    int padv = 0;
+    if (col && q == 0) {
+        a.cnt[e] = total;
         if (a.mode == EP_MODE_COMPACT) {
-            padv = (run + a.A - 1) / a.A * a.A;
+            padv = (total + a.A - 1) / a.A * a.A;
         } else {
-            padv = run < a.C ? run : a.C;
-            if (run > a.C) f |= EP_ERRFLAG_OVERFLOW;
+            padv = total < a.C ? total : a.C;
+            if (total > a.C) f |= EP_ERRFLAG_OVERFLOW;
         }
         a.pad[e] = padv;
     }
-    int total;
-    const int excl = block_exclusive_scan(padv, tmp, &total);
-    if (tid < a.E) s_off[tid] = a.mode == EP_MODE_COMPACT ? excl : tid * a.C;
-    if (tid == 0) s_off[a.E] = a.mode == EP_MODE_COMPACT ? total : a.E * a.C;
+    int sum_pad;
+    const int excl = block_exclusive_scan(padv, tmp, &sum_pad);  // q != 0 threads add 0
+    if (col && q == 0) s_off[e] = a.mode == EP_MODE_COMPACT ? excl : e * a.C;
+    if (tid == 0) s_off[a.E] = a.mode == EP_MODE_COMPACT ? sum_pad : a.E * a.C;
     __syncthreads();
-    for (int e = tid; e <= a.E; e += 1024) a.expert_off[e] = s_off[e];
+    for (int i = tid; i <= a.E; i += 1024) a.expert_off[i] = s_off[i];
     for (int d = tid; d <= a.D; d += 1024) a.dest_off[d] = s_off[d * a.epd];
-    for (int d = tid; d < a.D; d += 1024) {
-        int s = 0;
-        for (int b = 0; b < a.nblk; ++b) s += a.dpart[(int64_t)b * a.D + d];
-        a.dest_tokens[d] = s;
-    }
-    // OR of the flags over the block
+    for (int d = tid; d < a.D; d += 1024) a.dest_tokens[d] = s_dest[d];
     const uint32_t fo = (uint32_t)__syncthreads_or(f & EP_ERRFLAG_BAD_ID);
     const uint32_t fv = (uint32_t)__syncthreads_or(f & EP_ERRFLAG_OVERFLOW);
     if (tid == 0) a.err_flags[0] = (fo ? EP_ERRFLAG_BAD_ID : 0u) | (fv ? EP_ERRFLAG_OVERFLOW : 0u);
@@ -183,40 +222,51 @@ __device__ __forceinline__ void emit_padding_meta(const LayoutArgs& a, const int
     }
 }
 
-template <int NW, int IT>
-__global__ __launch_bounds__(NW * 64) void k_layout_assign(LayoutArgs a) {
+// Stable slots: rank inside the wave's group (ballots), plus the counts of
+// the earlier waves of the block, plus the block's base inside the expert.
+__global__ __launch_bounds__(kLayoutWaves * 64) void k_layout_assign(LayoutArgs a) {
     extern __shared__ int32_t lds[];
-    int32_t* wcnt = lds;  // [NW][E]
+    int32_t* bbase = lds;                              // [E] block base + expert offset
+    uint16_t* wc = (uint16_t*)(lds + a.E);             // [kLayoutWaves][E] per-wave counts
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < NW * a.E; i += NW * 64) lds[i] = 0;
+    for (int i = tid; i < kLayoutWaves * a.E; i += blockDim.x) wc[i] = 0;
+    for (int i = tid; i < a.E; i += blockDim.x)
+        bbase[i] = a.bpart[(int64_t)blockIdx.x * a.E + i] + (a.mode == EP_MODE_COMPACT ? a.expert_off[i] : 0);
+    const int64_t base = ((int64_t)blockIdx.x * kLayoutWaves + w) * kWave;
+    bool v, bad;
+    const int e = load_group(a, base, v, bad);
+    const uint64_t peers = match_peers(e, v, a.nbits);
+    const int rank = __popcll(peers & lanes_below(lane));
     __syncthreads();
-    const int64_t base = ((int64_t)blockIdx.x * NW + w) * (IT * kWave);
-    int ids[IT], rank[IT];
-    bool val[IT];
-    wave_rank<IT, false>(a, base, ids, val, rank, wcnt + w * a.E, nullptr);
+    if (v && (int)(__ffsll((long long)peers) - 1) == lane) wc[w * a.E + e] = (uint16_t)__popcll(peers);
     __syncthreads();
-    // wave bases inside the block, offset by the block's base in each expert
-    for (int e = tid; e < a.E; e += NW * 64) {
-        int run = a.bpart[(int64_t)blockIdx.x * a.E + e];
+    for (int i = tid; i < a.E; i += blockDim.x) {
+        int run = 0;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const int c = wcnt[ww * a.E + e];
-            wcnt[ww * a.E + e] = run;
+        for (int ww = 0; ww < kLayoutWaves; ++ww) {
+            const int c = wc[ww * a.E + i];
+            wc[ww * a.E + i] = (uint16_t)run;
             run += c;
         }
     }
     __syncthreads();
-    const int64_t P = (int64_t)a.T * a.k;
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int64_t p = base + it * kWave + lane;
-        if (p >= P) continue;
-        if (!val[it]) {
+    const int64_t p = base + lane;
+    if (p < (int64_t)a.T * a.k) {
+        if (!v) {
             a.slot[p] = -1;
-            continue;
+        } else {
+            const int r = bbase[e] + wc[w * a.E + e] + rank;   // COMPACT: row; FIXED: rank in expert
+            int32_t s;
+            if (a.mode == EP_MODE_COMPACT)
+                s = r;
+            else
+                s = r < a.C ? e * a.C + r : -1;
+            a.slot[p] = s;
+            if (s >= 0) {
+                a.row_src[s] = (int32_t)p;
+                if (a.w) a.row_w[s] = a.w[p];
+            }
         }
-        const int e = ids[it];
-        emit_slot(a, p, e, wcnt[w * a.E + e] + rank[it], a.mode == EP_MODE_COMPACT ? a.expert_off[e] : 0);
     }
     emit_padding_meta(a, a.expert_off, a.cnt, blockIdx.x, gridDim.x);
 }
@@ -298,17 +348,17 @@ hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream) {
             hipLaunchKernelGGL(k_layout_small<4>, dim3(1), dim3(1024), lds, stream, a);
         return hipGetLastError();
     }
-    const size_t lds_count = sizeof(int32_t) * (kLayoutWaves * a.E + a.D);
-    const size_t lds_assign = sizeof(int32_t) * (kLayoutWaves * a.E);
-    hipLaunchKernelGGL((k_layout_count<kLayoutWaves, kLayoutIters>), dim3(a.nblk), dim3(kLayoutWaves * 64),
-                       lds_count, stream, a);
+    const size_t lds_count = sizeof(int32_t) * (a.E + a.D);
+    const size_t lds_assign = sizeof(int32_t) * a.E + sizeof(uint16_t) * kLayoutWaves * a.E;
+    hipLaunchKernelGGL(k_layout_count, dim3(a.nblk), dim3(kLayoutWaves * 64), lds_count, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(1024), 0, stream, a);
+    int tpe = 1;
+    while (tpe < 16 && (tpe * 2) * a.E <= 1024) tpe *= 2;
+    hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(1024), 0, stream, a, tpe);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_layout_assign<kLayoutWaves, kLayoutIters>), dim3(a.nblk), dim3(kLayoutWaves * 64),
-                       lds_assign, stream, a);
+    hipLaunchKernelGGL(k_layout_assign, dim3(a.nblk), dim3(kLayoutWaves * 64), lds_assign, stream, a);
     return hipGetLastError();
 }
 
