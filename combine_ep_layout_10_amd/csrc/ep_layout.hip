@@ -129,21 +129,27 @@ __global__ __launch_bounds__(1024) void k_layout_scan(LayoutArgs a, int tpe) {
     __shared__ int32_t s_dest[1024];
     __shared__ int tmp[17];
     const int tid = threadIdx.x;
-    uint32_t f = 0;
-    for (int b = tid; b < a.nblk; b += 1024) f |= a.fpart[b];
-    for (int d = tid; d < a.D; d += 1024) s_dest[d] = 0;
-    __syncthreads();
-    for (int i = tid; i < a.nblk * a.D; i += 1024) atomicAdd(&s_dest[i % a.D], a.dpart[i]);
-
     const int e = tid / tpe, q = tid % tpe;
     const bool col = e < a.E;
     const int per = (a.nblk + tpe - 1) / tpe;
     const int b0 = q * per, b1 = min(a.nblk, b0 + per);
+    // Every global load is issued before the first barrier: one round trip.
     int cache[16];
-    int sum = 0;
     if (col) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) cache[u] = (b0 + u < b1) ? a.bpart[(int64_t)(b0 + u) * a.E + e] : 0;
+    }
+    uint32_t f = 0;
+    for (int b = tid; b < a.nblk; b += 1024) f |= a.fpart[b];
+    const int ndp = a.nblk * a.D;
+    const int dval = tid < ndp ? a.dpart[tid] : 0;
+    for (int d = tid; d < a.D; d += 1024) s_dest[d] = 0;
+    __syncthreads();
+    if (tid < ndp) atomicAdd(&s_dest[tid % a.D], dval);
+    for (int i = tid + 1024; i < ndp; i += 1024) atomicAdd(&s_dest[i % a.D], a.dpart[i]);
+
+    int sum = 0;
+    if (col) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) sum += cache[u];
         for (int b = b0 + 16; b < b1; ++b) sum += a.bpart[(int64_t)b * a.E + e];
@@ -226,15 +232,26 @@ __device__ __forceinline__ void emit_padding_meta(const LayoutArgs& a, const int
 // the earlier waves of the block, plus the block's base inside the expert.
 __global__ __launch_bounds__(kLayoutWaves * 64) void k_layout_assign(LayoutArgs a) {
     extern __shared__ int32_t lds[];
-    int32_t* bbase = lds;                              // [E] block base + expert offset
-    uint16_t* wc = (uint16_t*)(lds + a.E);             // [kLayoutWaves][E] per-wave counts
+    int32_t* bbase = lds;                              // [E] block base (+ expert offset)
+    int32_t* s_off = bbase + a.E;                      // [E+1] expert offsets
+    int32_t* s_cnt = s_off + a.E + 1;                  // [E] counts
+    uint16_t* wc = (uint16_t*)(s_cnt + a.E);           // [kLayoutWaves][E] per-wave counts
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < kLayoutWaves * a.E; i += blockDim.x) wc[i] = 0;
-    for (int i = tid; i < a.E; i += blockDim.x)
-        bbase[i] = a.bpart[(int64_t)blockIdx.x * a.E + i] + (a.mode == EP_MODE_COMPACT ? a.expert_off[i] : 0);
+    // Every global load is issued before the first barrier: one round trip.
     const int64_t base = ((int64_t)blockIdx.x * kLayoutWaves + w) * kWave;
+    const int64_t p = base + lane;
+    const bool live = p < (int64_t)a.T * a.k;
     bool v, bad;
     const int e = load_group(a, base, v, bad);
+    const float wp = (a.w != nullptr && live) ? a.w[p] : 0.0f;
+    for (int i = tid; i < a.E; i += blockDim.x) {
+        const int off = a.expert_off[i];
+        bbase[i] = a.bpart[(int64_t)blockIdx.x * a.E + i] + (a.mode == EP_MODE_COMPACT ? off : 0);
+        s_off[i] = off;
+        s_cnt[i] = a.cnt[i];
+    }
+    if (tid == 0) s_off[a.E] = a.expert_off[a.E];
+    for (int i = tid; i < kLayoutWaves * a.E; i += blockDim.x) wc[i] = 0;
     const uint64_t peers = match_peers(e, v, a.nbits);
     const int rank = __popcll(peers & lanes_below(lane));
     __syncthreads();
@@ -250,8 +267,7 @@ __global__ __launch_bounds__(kLayoutWaves * 64) void k_layout_assign(LayoutArgs 
         }
     }
     __syncthreads();
-    const int64_t p = base + lane;
-    if (p < (int64_t)a.T * a.k) {
+    if (live) {
         if (!v) {
             a.slot[p] = -1;
         } else {
@@ -264,11 +280,11 @@ __global__ __launch_bounds__(kLayoutWaves * 64) void k_layout_assign(LayoutArgs 
             a.slot[p] = s;
             if (s >= 0) {
                 a.row_src[s] = (int32_t)p;
-                if (a.w) a.row_w[s] = a.w[p];
+                if (a.w) a.row_w[s] = wp;
             }
         }
     }
-    emit_padding_meta(a, a.expert_off, a.cnt, blockIdx.x, gridDim.x);
+    emit_padding_meta(a, s_off, s_cnt, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- one block
@@ -349,7 +365,7 @@ hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream) {
         return hipGetLastError();
     }
     const size_t lds_count = sizeof(int32_t) * (a.E + a.D);
-    const size_t lds_assign = sizeof(int32_t) * a.E + sizeof(uint16_t) * kLayoutWaves * a.E;
+    const size_t lds_assign = sizeof(int32_t) * (3 * a.E + 1) + sizeof(uint16_t) * kLayoutWaves * a.E;
     hipLaunchKernelGGL(k_layout_count, dim3(a.nblk), dim3(kLayoutWaves * 64), lds_count, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -52,14 +52,20 @@ class Config:
         return n
 
     def recv_rows_bound(self) -> int:
-        n = F.ep_recv_rows_bound(self.c())
-        if n < 0:
-            raise F.EPError(F.EP_ERR_INVALID_ARG, "ep_recv_rows_bound", F.last_error_message())
+        n = _ROWS_BOUND.get(self)
+        if n is None:
+            n = F.ep_recv_rows_bound(self.c())
+            if n < 0:
+                raise F.EPError(F.EP_ERR_INVALID_ARG, "ep_recv_rows_bound", F.last_error_message())
+            _ROWS_BOUND[self] = n
         return n
 
 
+_ROWS_BOUND = {}
+
+
 def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+    return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -151,6 +157,16 @@ class Handle:
         return F.ep_handle_check(self.c, _stream())
 
 
+_C_CONFIG = {}
+
+
+def _c_config(cfg: Config) -> F.ep_config:
+    c = _C_CONFIG.get(cfg)
+    if c is None:
+        c = _C_CONFIG[cfg] = cfg.c()
+    return c
+
+
 def new_workspace(cfg: Config, device="cuda") -> torch.Tensor:
     return torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device=device)
 
@@ -165,7 +181,7 @@ def layout(cfg: Config, topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor] =
         raise ValueError("topk_w must match topk_idx")
     if workspace is None:
         workspace = new_workspace(cfg, topk_idx.device)
-    h = F.ep_layout(cfg.c(), T, _dev(topk_idx, "topk_idx", idx_dtype), _opt(topk_w, "topk_w", torch.float32),
+    h = F.ep_layout(_c_config(cfg), T, _dev(topk_idx, "topk_idx", idx_dtype), _opt(topk_w, "topk_w", torch.float32),
                     _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
     return Handle(cfg, h, workspace)
 
