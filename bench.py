@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    p.add_argument("--no-copy-ceiling", action="store_true",
+                   help="skip timing a plain 1 GiB device-to-device copy for reference")
     return p.parse_args()
 
 
@@ -193,6 +195,24 @@ def main():
                 "algorithmic_bytes_per_launch": nbytes[dominant],
                 "avg_launch_us": round((com_ms if dominant == "combine" else dis_ms) * 1e3, 2)}
 
+    copy_ceiling = None
+    if not args.no_copy_ceiling:
+        # Reference only: a plain 1 GiB device-to-device copy (read + write).
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            b.copy_(a)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        copy_ceiling = round(2 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+        del a, b
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -230,6 +250,7 @@ def main():
             "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
             "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
             "bytes": nbytes, "kernel_hash": khash,
+            "copy_1GiB_GBps": copy_ceiling,
         },
     }
     print(json.dumps(res), flush=True)
