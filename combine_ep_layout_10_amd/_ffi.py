@@ -77,6 +77,8 @@ _SIGNATURES = {
     "ep_recv_rows_bound": (ctypes.c_int64, [ctypes.POINTER(ep_config)]),
     "ep_layout": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
                                  ctypes.POINTER(ep_handle), _P]),
+    "ep_dispatch_forward": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
+                                           ctypes.c_int, _P, _P, _P, _P, ctypes.POINTER(ep_handle), _P]),
     "ep_dispatch": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int, _P, _P, _P, _P, _P]),
     "ep_combine": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),
@@ -132,6 +134,16 @@ def ep_layout(cfg: ep_config, num_tokens: int, topk_idx: int, topk_w, workspace:
     h = ep_handle()
     _check(lib().ep_layout(ctypes.byref(cfg), int(num_tokens), topk_idx, topk_w, workspace,
                            int(workspace_bytes), ctypes.byref(h), stream), "ep_layout")
+    return h
+
+
+def ep_dispatch_forward(cfg: ep_config, num_tokens: int, topk_idx: int, topk_w, workspace: int,
+                        workspace_bytes: int, dtype: int, x: int, x_scales, recv: int, recv_scales,
+                        stream: int) -> ep_handle:
+    h = ep_handle()
+    _check(lib().ep_dispatch_forward(ctypes.byref(cfg), int(num_tokens), topk_idx, topk_w, workspace,
+                                     int(workspace_bytes), int(dtype), x, x_scales, recv, recv_scales,
+                                     ctypes.byref(h), stream), "ep_dispatch_forward")
     return h
 
 

@@ -104,8 +104,9 @@ ep_status check_handle(const ep_handle* h) {
     return EP_OK;
 }
 
-ep_status do_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales, const float* pair_w,
-                      void* recv, float* recv_scales, hipStream_t stream) {
+// Checks a dispatch and fills its kernel arguments; enqueues nothing.
+ep_status prepare_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales,
+                           const float* pair_w, void* recv, float* recv_scales, ep::DispatchArgs* out, int* kind) {
     ep_status s = check_handle(h);
     if (s != EP_OK) return s;
     const ep_config& c = h->cfg;
@@ -123,7 +124,7 @@ ep_status do_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const f
         return fail(EP_ERR_INVALID_ARG, "recv_scales is required for FP8 dispatch");
     if (dtype == EP_FP8_PREQUANT && T > 0 && (x_scales == nullptr || !aligned(x_scales, 4)))
         return fail(EP_ERR_INVALID_ARG, "x_scales is required for EP_FP8_PREQUANT");
-    ep::DispatchArgs a;
+    ep::DispatchArgs& a = *out;
     a.x = x;
     a.x_scales = x_scales;
     a.recv = recv;
@@ -141,13 +142,21 @@ ep_status do_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const f
     a.pad_blocks_per_expert = a.zero_pad ? (c.expert_alignment - 1 + ep::kPadRowsPerBlock - 1) / ep::kPadRowsPerBlock : 0;
     a.npad_blocks = a.pad_blocks_per_expert * c.num_experts;
     if (a.pad_blocks_per_expert == 0) a.pad_blocks_per_expert = 1;  // never divided by when npad_blocks == 0
-    int kind;
     if (dtype == EP_BF16)
-        kind = pair_w ? ep::kDispatchBf16Weighted : ep::kDispatchBf16;
+        *kind = pair_w ? ep::kDispatchBf16Weighted : ep::kDispatchBf16;
     else if (dtype == EP_FP8_QUANTIZE)
-        kind = ep::kDispatchFp8Quant;
+        *kind = ep::kDispatchFp8Quant;
     else
-        kind = ep::kDispatchFp8Copy;
+        *kind = ep::kDispatchFp8Copy;
+    return EP_OK;
+}
+
+ep_status do_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales, const float* pair_w,
+                      void* recv, float* recv_scales, hipStream_t stream) {
+    ep::DispatchArgs a;
+    int kind = 0;
+    ep_status s = prepare_dispatch(h, dtype, x, x_scales, pair_w, recv, recv_scales, &a, &kind);
+    if (s != EP_OK) return s;
     hipError_t e = ep::launch_dispatch(kind, a, stream);
     if (e != hipSuccess) return hip_fail(e, "dispatch launch");
     return EP_OK;
@@ -178,25 +187,11 @@ ep_status do_combine(const ep_handle* h, const void* y, const float* w, void* ou
     return EP_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ep_workspace_bytes(const ep_config* cfg) {
-    if (check_config(cfg) != EP_OK) return 0;
-    return ws_map(*cfg).total;
-}
-
-int64_t ep_recv_rows_bound(const ep_config* cfg) {
-    if (check_config(cfg) != EP_OK) return -1;
-    return rows_bound(*cfg);
-}
-
-ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
-                    void* workspace, size_t workspace_bytes, ep_handle* out, void* stream) {
+// Checks a layout, builds its handle and kernel arguments; enqueues nothing.
+ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
+                         void* workspace, size_t workspace_bytes, ep_handle* out, ep::LayoutArgs* args, bool* small_out) {
     ep_status s = check_config(cfg);
     if (s != EP_OK) return s;
-    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out handle is NULL");
     if (num_tokens < 0 || num_tokens > cfg->max_tokens)
         return fail(EP_ERR_INVALID_ARG, "num_tokens %d outside [0, %d]", num_tokens, cfg->max_tokens);
     if (num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, cfg->idx_bits / 8)))
@@ -229,7 +224,7 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
     if (nblk < 1) nblk = 1;  // a layout of zero pairs still writes zero counts
     h.num_blocks = small ? 1 : nblk;
 
-    ep::LayoutArgs a;
+    ep::LayoutArgs& a = *args;
     a.idx = topk_idx;
     a.w = topk_w;
     a.idx_bits = cfg->idx_bits;
@@ -257,8 +252,67 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
     a.bpart = (int32_t*)(ws + m.bpart);
     a.dpart = (int32_t*)(ws + m.dpart);
     a.fpart = (uint32_t*)(ws + m.fpart);
+    *small_out = small;
+    *out = h;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_config* cfg) {
+    if (check_config(cfg) != EP_OK) return 0;
+    return ws_map(*cfg).total;
+}
+
+int64_t ep_recv_rows_bound(const ep_config* cfg) {
+    if (check_config(cfg) != EP_OK) return -1;
+    return rows_bound(*cfg);
+}
+
+ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
+                    void* workspace, size_t workspace_bytes, ep_handle* out, void* stream) {
+    ep_handle h;
+    ep::LayoutArgs a;
+    bool small = false;
+    ep_status s = check_config(cfg);
+    if (s != EP_OK) return s;
+    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out handle is NULL");
+    s = prepare_layout(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, &h, &a, &small);
+    if (s != EP_OK) return s;
     hipError_t e = ep::launch_layout(a, small, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "layout launch");
+    *out = h;
+    return EP_OK;
+}
+
+ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
+                              void* workspace, size_t workspace_bytes, ep_dtype dtype, const void* x,
+                              const float* x_scales, void* recv, float* recv_scales, ep_handle* out, void* stream) {
+    ep_handle h;
+    ep::LayoutArgs la;
+    bool small = false;
+    ep_status s = check_config(cfg);
+    if (s != EP_OK) return s;
+    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out handle is NULL");
+    s = prepare_layout(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, &h, &la, &small);
+    if (s != EP_OK) return s;
+    ep::DispatchArgs da;
+    int kind = 0;
+    s = prepare_dispatch(&h, dtype, x, x_scales, nullptr, recv, recv_scales, &da, &kind);
+    if (s != EP_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (small && ep::fused_layout_dispatch_fits((int64_t)num_tokens * cfg->num_topk, cfg->num_experts)) {
+        e = ep::launch_layout_dispatch_small(kind, la, da, st);
+        if (e != hipSuccess) return hip_fail(e, "layout + dispatch launch");
+    } else {
+        e = ep::launch_layout(la, small, st);
+        if (e != hipSuccess) return hip_fail(e, "layout launch");
+        e = ep::launch_dispatch(kind, da, st);
+        if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+    }
     *out = h;
     return EP_OK;
 }

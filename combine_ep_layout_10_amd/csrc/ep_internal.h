@@ -15,6 +15,9 @@ constexpr int kLayoutPairsPerBlock = kLayoutWaves * kWave;  // 1024
 // Single-block layout limits.
 constexpr int kSmallMaxPairs = 4096;
 constexpr int kSmallMaxExperts = 512;
+// Largest per-block count matrix (blocks x experts) that every assign block
+// reduces on its own instead of waiting for a one-block scan launch.
+constexpr int kInlineScanMaxCells = 32768;
 // Limits checked by the host API.
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
@@ -27,6 +30,7 @@ struct LayoutArgs {
     int nbits;  // bits needed to hold any expert id
     int epd;    // experts per destination
     int nblk;   // multi-block grid size
+    int tpe;    // threads per expert column when reducing per-block counts
     int32_t* cnt;
     int32_t* pad;
     int32_t* expert_off;
@@ -75,5 +79,8 @@ constexpr int kPadRowsPerBlock = 16;
 hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
 hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// Single-launch layout + dispatch (unweighted kinds) for small batches.
+bool fused_layout_dispatch_fits(int64_t pairs, int E);
+hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, hipStream_t stream);
 
 }  // namespace ep

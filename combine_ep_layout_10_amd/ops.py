@@ -3,6 +3,7 @@ stream, every step runs in the HIP kernels behind include/ep.h.
 
 Mapping to the DeepEP README ("Interfaces and examples"):
   layout + dispatch            -> dispatch_forward (recv_x, handle)
+  dispatch_forward             -> the same in one call (one launch for small batches)
   Handle.row_src / row_w       -> recv_topk_idx / recv_topk_weights (per row)
   Handle.pad (read_counts)     -> handle.num_recv_tokens_per_expert_list
   combine                      -> combine_forward
@@ -213,6 +214,41 @@ def dispatch(h: Handle, x: torch.Tensor, dtype: int = BF16, x_scales: Optional[t
                   _opt(recv_scales, "recv_scales", torch.float32),
                   _stream())
     return (recv, recv_scales) if dtype != BF16 else recv
+
+
+def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype: int = BF16,
+                     topk_w: Optional[torch.Tensor] = None, x_scales: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, recv: Optional[torch.Tensor] = None,
+                     recv_scales: Optional[torch.Tensor] = None):
+    """Layout + dispatch in one call (README dispatch_forward). Returns
+    (handle, recv) or (handle, recv, recv_scales) for the FP8 types."""
+    idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
+    T, H, R = int(topk_idx.shape[0]), cfg.hidden, cfg.recv_rows_bound()
+    if topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+        raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
+    if topk_w is not None and tuple(topk_w.shape) != tuple(topk_idx.shape):
+        raise ValueError("topk_w must match topk_idx")
+    _need(x, (T, H), "x")
+    if dtype == FP8_PREQUANT:
+        _need(x_scales, (T, H // 128), "x_scales")
+    if workspace is None:
+        workspace = new_workspace(cfg, topk_idx.device)
+    fp8 = dtype != BF16
+    if recv is None:
+        recv = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=x.device)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=x.device)
+    _need(recv, (R, H), "recv")
+    if fp8:
+        _need(recv_scales, (R, H // 128), "recv_scales")
+    xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
+    c = F.ep_dispatch_forward(_c_config(cfg), T, _dev(topk_idx, "topk_idx", idx_dtype),
+                              _opt(topk_w, "topk_w", torch.float32), _dev(workspace, "workspace", torch.uint8),
+                              workspace.numel(), dtype, _dev(x, "x", xdt), _opt(x_scales, "x_scales", torch.float32),
+                              _dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16),
+                              _opt(recv_scales, "recv_scales", torch.float32), _stream())
+    h = Handle(cfg, c, workspace)
+    return (h, recv, recv_scales) if fp8 else (h, recv)
 
 
 def combine(h: Handle, y: torch.Tensor, topk_w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,

@@ -167,6 +167,22 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
                     const float* topk_w, void* workspace, size_t workspace_bytes,
                     ep_handle* out, void* stream);
 
+/* Layout and dispatch in one call: the README's dispatch_forward, which
+ * builds the handle (per-expert counts, padded offsets, stable slots) and
+ * moves the hidden states in the same call. Arguments are those of
+ * ep_layout followed by those of ep_dispatch; every argument of both is
+ * checked before anything is enqueued. The results (handle contents, recv,
+ * recv_scales) are bit-identical to ep_layout followed by ep_dispatch.
+ * Small batches (num_tokens * k <= 4096 and E <= 512, the decode sizes of
+ * README "Example use in inference decoding") take a single kernel launch:
+ * every block recomputes the small layout in LDS, so no block waits on
+ * another. Larger batches enqueue the layout kernels and then the dispatch
+ * kernel. Never synchronises. */
+ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
+                              const float* topk_w, void* workspace, size_t workspace_bytes,
+                              ep_dtype dtype, const void* x, const float* x_scales, void* recv,
+                              float* recv_scales, ep_handle* out, void* stream);
+
 /* Dispatch on an existing handle (README dispatch_forward, or dispatch with a
  * cached handle: no layout work, no synchronisation).
  *   x          device [T, hidden]: bf16 (EP_BF16, EP_FP8_QUANTIZE) or E4M3FN

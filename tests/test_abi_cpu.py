@@ -130,3 +130,33 @@ def test_struct_sizes_match_header():
     # ep_config: 10 x 4 bytes; ep_handle: config + 2 ints + 10 pointers
     assert ctypes.sizeof(F.ep_config) == 40
     assert ctypes.sizeof(F.ep_handle) == 40 + 8 + 10 * 8
+
+
+def test_dispatch_forward_argument_errors():
+    """Layout and dispatch arguments are all checked before anything is
+    enqueued (every call below fails a check; no pointer is dereferenced)."""
+    c = cfg()
+    lib = F.lib()
+    h = F.ep_handle()
+    need = F.ep_workspace_bytes(c)
+    fake = ctypes.c_void_p(1 << 20)
+    f = lib.ep_dispatch_forward
+    assert f(None, 4, fake, None, fake, need, F.EP_BF16, fake, None, fake, None, ctypes.byref(h), None) \
+        == F.EP_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), 65, fake, None, fake, need, F.EP_BF16, fake, None, fake, None, ctypes.byref(h),
+             None) == F.EP_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), 4, fake, None, fake, need - 256, F.EP_BF16, fake, None, fake, None,
+             ctypes.byref(h), None) == F.EP_ERR_WORKSPACE
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, 7, fake, None, fake, None, ctypes.byref(h),
+             None) == F.EP_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_BF16, None, None, fake, None, ctypes.byref(h),
+             None) == F.EP_ERR_INVALID_ARG                                     # x NULL
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_BF16, fake, None, None, None, ctypes.byref(h),
+             None) == F.EP_ERR_INVALID_ARG                                     # recv NULL
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_FP8_QUANTIZE, fake, None, fake, None,
+             ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG                    # recv_scales NULL
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_FP8_PREQUANT, fake, None, fake, fake,
+             ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG                    # x_scales NULL
+    assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_BF16, fake, None, fake, None, None,
+             None) == F.EP_ERR_INVALID_ARG                                     # out NULL
+    assert "out handle" in F.last_error_message()

@@ -20,10 +20,12 @@ if torch.cuda.is_available():
 
 
 def _run_small(T, H, E, k, A=1, D=1, C=0, mode=0, seed=0, masked=0.0, bad=0.0, distinct=True,
-               idx_bits=64, flags=0, dispatch="bf16", weights=True):
-    """Random small case through every stage, checked against the oracle."""
-    log("case T=%d H=%d E=%d k=%d A=%d D=%d C=%d mode=%d idx_bits=%d dispatch=%s seed=%d"
-        % (T, H, E, k, A, D, C, mode, idx_bits, dispatch, seed))
+               idx_bits=64, flags=0, dispatch="bf16", weights=True, forward=False):
+    """Random small case through every stage, checked against the oracle.
+    forward=True builds the layout and dispatches with one ep_dispatch_forward
+    call instead of ep_layout + ep_dispatch."""
+    log("case T=%d H=%d E=%d k=%d A=%d D=%d C=%d mode=%d idx_bits=%d dispatch=%s seed=%d forward=%d"
+        % (T, H, E, k, A, D, C, mode, idx_bits, dispatch, seed, forward))
     rng = np.random.default_rng(seed)
     idx = random_routing_table(rng, T, E, k, masked_frac=masked, bad_frac=bad, distinct=distinct)
     if idx_bits == 32:
@@ -33,26 +35,36 @@ def _run_small(T, H, E, k, A=1, D=1, C=0, mode=0, seed=0, masked=0.0, bad=0.0, d
     lay = oracle.layout(mode, T, E, k, A, D, C, idx, w)
     cfg = ops.Config(max_tokens=max(T, 1), hidden=H, num_experts=E, num_topk=k, num_dests=D,
                      expert_alignment=A, capacity=C, mode=mode, idx_bits=idx_bits, flags=flags)
-    h = ops.layout(cfg, to_dev(idx), None if w is None else to_dev(w))
-    compare_layout(h, lay, weights=w is not None)
     R = cfg.recv_rows_bound()
+    dev_w = None if w is None else to_dev(w)
+    if dispatch == "bf16":
+        recv = torch.full((R, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        rs = None
+    else:
+        recv = torch.full((R, H), 0xEE, dtype=torch.uint8, device="cuda")
+        rs = torch.full((R, H // 128), -7.0, dtype=torch.float32, device="cuda")
+    dt = ops.BF16 if dispatch == "bf16" else ops.FP8_QUANTIZE
+    if forward:
+        h = ops.dispatch_forward(cfg, to_dev(idx), to_dev_bf16(x), dt, topk_w=dev_w, recv=recv, recv_scales=rs)[0]
+    else:
+        h = ops.layout(cfg, to_dev(idx), dev_w)
+    compare_layout(h, lay, weights=w is not None)
     rows = written_rows(lay)
     zero_pad = not (flags & ops.FLAG_NO_ZERO_PAD)
     if mode == oracle.MODE_COMPACT and not zero_pad:
         rows = rows[lay["row_src"][rows] >= 0]
     if dispatch == "bf16":
         ref = oracle.dispatch_bf16(lay, x, k, zero_pad=zero_pad)
-        recv = torch.full((R, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-        ops.dispatch(h, to_dev_bf16(x), ops.BF16, recv=recv)
+        if not forward:
+            ops.dispatch(h, to_dev_bf16(x), ops.BF16, recv=recv)
         got = bf16_host(recv)
         assert np.array_equal(got[rows], ref[rows])
         untouched = np.setdiff1d(np.arange(R), rows)
         assert np.all(got[untouched] == 0xFFFF)
     else:
         q, s = oracle.dispatch_fp8(lay, x, k, zero_pad=zero_pad)
-        recv = torch.full((R, H), 0xEE, dtype=torch.uint8, device="cuda")
-        rs = torch.full((R, H // 128), -7.0, dtype=torch.float32, device="cuda")
-        ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE, recv=recv, recv_scales=rs)
+        if not forward:
+            ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE, recv=recv, recv_scales=rs)
         assert np.array_equal(host(recv)[rows], q[rows])
         assert np.array_equal(host(rs)[rows].view(np.uint32), s[rows].view(np.uint32))
         untouched = np.setdiff1d(np.arange(R), rows)
@@ -82,7 +94,10 @@ def test_tiny_hand_example():
     (819, 64, 5, 128, 4),        # P = 4095: single-block path
     (820, 64, 5, 128, 4),        # P = 4100: multi-block path
     (2049, 600, 2, 8, 6),        # E > 512: multi-block path with few pairs
-    (5000, 1024, 7, 3, 32),      # largest E
+    (5000, 1024, 7, 3, 32),      # largest E; per-block count matrix too big to re-read: 3 kernels
+    (16384, 256, 8, 128, 8),     # 128 count blocks x 256 experts: the largest matrix reduced inline
+    (16400, 256, 8, 128, 8),     # 129 count blocks: one-block scan launch
+    (40000, 256, 4, 16, 8),      # many count blocks, 3 kernels
 ])
 def test_random_layouts(T, E, k, A, D):
     _run_small(T, 64, E, k, A=A, D=D, seed=T + E)
@@ -107,6 +122,10 @@ def test_fixed_capacity_and_overflow():
     assert lay["flags"] == oracle.FLAG_OVERFLOW and h.check() == oracle.FLAG_OVERFLOW
     h, lay = _run_small(3000, 128, 8, 3, mode=1, C=500, seed=9)     # multi-block, overflow
     assert h.check() == oracle.FLAG_OVERFLOW
+    h, lay = _run_small(12000, 64, 1024, 4, mode=1, C=40, seed=16)  # 3-kernel layout, overflow
+    assert lay["flags"] == oracle.FLAG_OVERFLOW and h.check() == oracle.FLAG_OVERFLOW
+    h, lay = _run_small(9000, 64, 1000, 5, A=4, D=8, seed=17, masked=0.1, bad=0.01, distinct=False)
+    assert h.check() == oracle.FLAG_BAD_ID                             # 3-kernel layout, bad ids
 
 
 def test_no_zero_pad_flag():
@@ -144,6 +163,102 @@ def test_argument_errors_enqueue_nothing():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(Exception):
         ops.layout(cfg, idx[:4], workspace=ws)              # workspace too small
+
+
+# ---------------------------------------------------------------- one-call dispatch_forward
+
+@pytest.mark.parametrize("T,E,k,A,D,C,mode,dispatch,masked,bad", [
+    (128, 16, 2, 1, 1, 0, 0, "bf16", 0.0, 0.0),          # tiny shape, single launch
+    (128, 256, 8, 1, 1, 128, 1, "fp8", 0.0, 0.0),        # decode shape (FIXED), single launch
+    (100, 64, 8, 16, 4, 0, 0, "fp8", 0.0, 0.0),          # padding rows cleared by the same launch
+    (128, 64, 8, 1, 1, 12, 1, "bf16", 0.0, 0.0),         # FIXED overflow
+    (129, 64, 8, 32, 2, 0, 0, "bf16", 0.0, 0.0),         # P = 1032: four groups per wave
+    (512, 512, 8, 8, 8, 0, 0, "fp8", 0.1, 0.02),         # P = 4096, E = 512: largest single launch
+    (513, 512, 8, 8, 8, 0, 0, "bf16", 0.0, 0.0),         # P = 4104: layout + dispatch launches
+    (300, 513, 2, 4, 3, 0, 0, "bf16", 0.0, 0.0),         # E = 513: layout + dispatch launches
+    (1, 16, 4, 4, 2, 0, 0, "fp8", 0.0, 0.0),             # one token
+])
+def test_dispatch_forward(T, E, k, A, D, C, mode, dispatch, masked, bad):
+    H = 7168 if (T, E) == (128, 256) else 256
+    h, lay = _run_small(T, H, E, k, A=A, D=D, C=C, mode=mode, seed=T * 7 + E, masked=masked, bad=bad,
+                        distinct=masked == 0.0, dispatch=dispatch, forward=True)
+    assert h.check() == lay["flags"]
+
+
+def test_dispatch_forward_prequant_and_empty():
+    rng = np.random.default_rng(21)
+    T, H, E, k, A = 200, 256, 32, 4, 8
+    idx = random_routing_table(rng, T, E, k)
+    lay = oracle.layout(0, T, E, k, A, 1, 0, idx)
+    xq = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    q, s = oracle.dispatch_fp8_prequant(lay, xq, xs, k)
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A)
+    h, gq, gs = ops.dispatch_forward(cfg, to_dev(idx), to_dev(xq), ops.FP8_PREQUANT, x_scales=to_dev(xs))
+    compare_layout(h, lay, weights=False)
+    rows = np.arange(lay["rows"])
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
+    # empty batch: zero counts, nothing copied
+    cfg = ops.Config(max_tokens=16, hidden=128, num_experts=8, num_topk=2, expert_alignment=4)
+    idx = torch.zeros((0, 2), dtype=torch.int64, device="cuda")
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    h, recv = ops.dispatch_forward(cfg, idx, x)
+    cnt, pad, R = h.read_counts()
+    assert R == 0 and cnt.sum() == 0 and h.check() == 0
+
+
+def test_dispatch_forward_graph_replay():
+    """The decode step (one-call layout + dispatch, then combine) captured in
+    a HIP graph: every replay, with new routing copied in between, matches
+    the eager calls."""
+    wl = WORKLOADS["decode"]
+    cfg = cfg_of(wl)
+    R = cfg.recv_rows_bound()
+    rng = np.random.default_rng(22)
+    idx_s = torch.zeros((wl.T, wl.k), dtype=torch.int64, device="cuda")
+    w_s = torch.zeros((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    x_s = torch.zeros((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    y = to_dev_bf16(f32_to_bf16_bits(rng.standard_normal((R, wl.H)).astype(np.float32)))
+    ws = ops.new_workspace(cfg)
+    recv = torch.empty((R, wl.H), dtype=torch.uint8, device="cuda")
+    rs = torch.empty((R, wl.H // 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        h = ops.dispatch_forward(cfg, idx_s, x_s, ops.FP8_QUANTIZE, topk_w=w_s, workspace=ws, recv=recv,
+                                 recv_scales=rs)[0]
+        ops.combine(h, y, w_s, out=out)
+        return h
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                     # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = step()
+    for rep in range(3):
+        idx = np.stack([rng.permutation(wl.E)[:wl.k] for _ in range(wl.T)]).astype(np.int64)
+        w = rng.random((wl.T, wl.k)).astype(np.float32)
+        x = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
+        idx_s.copy_(to_dev(idx))
+        w_s.copy_(to_dev(w))
+        x_s.copy_(to_dev_bf16(x))
+        g.replay()
+        torch.cuda.synchronize()
+        got = (host(h.slot).copy(), host(recv).copy(), host(rs).copy(), bf16_host(out).copy())
+        step()                                     # eager, same inputs
+        torch.cuda.synchronize()
+        ref = (host(h.slot), host(recv), host(rs), bf16_host(out))
+        lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, idx, w)
+        assert np.array_equal(got[0], lay["slot"]), rep
+        rows = written_rows(lay)
+        assert np.array_equal(got[1][rows], ref[1][rows]), rep
+        assert np.array_equal(got[2][rows].view(np.uint32), ref[2][rows].view(np.uint32)), rep
+        assert np.array_equal(got[3], ref[3]), rep
 
 
 # ---------------------------------------------------------------- duals
