@@ -1,18 +1,21 @@
 """Benchmark: MoE layout -> dispatch -> combine on one MI355X.
 
-One step = one pass of the whole path over one batch: ep_layout (counts,
-offsets, stable slots), ep_dispatch (FP8 E4M3 1x128 quantise + copy for the
-V3 shape), ep_combine (weighted BF16 reduction of the expert outputs). The
-expert computation between dispatch and combine is not part of this path;
-combine reads a seeded synthetic expert output of the receive layout.
+One step = one pass of the whole path over one batch: ep_dispatch_forward
+(the layout — counts, offsets, stable slots — and the dispatch — FP8 E4M3
+1x128 quantise + copy for the V3 shape — in one call), then ep_combine
+(weighted BF16 reduction of the expert outputs). The expert computation
+between dispatch and combine is not part of this path; combine reads a
+seeded synthetic expert output of the receive layout.
 
 Inputs are seeded synthetic data resident in HBM before the timed region.
 Throughput is algorithmic bytes (the minimum each kernel must read and
 write) over time; `roofline` reports the dominant kernel against the
-MI355X HBM peak, timed with HIP events on the stream the kernels run on.
+MI355X HBM peak, timed with HIP events recorded around it inside the timed region, on the
+stream the kernels run on (--graph replays a captured step instead; the
+per-kernel times then come from an evented eager pass).
 `cpu_baseline` times the single-threaded CPU oracle on the same inputs.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--graph]
 """
 from __future__ import annotations
 
@@ -28,7 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch/combine effective GB/s + % of HBM peak, 8K tok×7168 top-8"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_device.h"]
+KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip", "ep_device.h",
+                  "ep_layout_dev.h", "ep_dispatch_dev.h"]
 
 
 def parse():
@@ -41,6 +45,8 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    p.add_argument("--graph", action="store_true",
+                   help="capture one step in a HIP graph and time K replays (launch-bound shapes)")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip timing a plain 1 GiB device-to-device copy for reference")
     return p.parse_args()
@@ -123,22 +129,27 @@ def main():
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(evs=None):
-        if evs:
-            evs[0].record(stream)
+    def step():
+        if fp8:
+            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
+        else:
+            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv)[0]
+        ops.combine(h, y, w, out=out)
+        return h
+
+    def step_split(evs):
+        """The same work as separate layout / dispatch / combine calls, with
+        an event between them."""
+        evs[0].record(stream)
         h = ops.layout(cfg, idx, w, workspace=ws)
-        if evs:
-            evs[1].record(stream)
+        evs[1].record(stream)
         if fp8:
             ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs)
         else:
             ops.dispatch(h, x, dtype, recv=recv)
-        if evs:
-            evs[2].record(stream)
+        evs[2].record(stream)
         ops.combine(h, y, w, out=out)
-        if evs:
-            evs[3].record(stream)
-        return h
+        evs[3].record(stream)
 
     h = step()
     cnt, pad, R = h.read_counts()
@@ -148,6 +159,7 @@ def main():
     P = int(cnt.sum()) if wl.mode == 0 else int(pad.sum())
     nbytes = algorithmic_bytes(wl, R, P, wl.dispatch)
     step_bytes = nbytes["layout"] + nbytes["dispatch"] + nbytes["combine"]
+    dominant = "combine" if nbytes["combine"] >= nbytes["dispatch"] else "dispatch"
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -157,43 +169,89 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
     print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
-    # Timed region: exactly K steps, nothing else on the stream.
+    # Timed region: exactly K steps. Eager steps carry one event pair around
+    # the dominant kernel (recorded on the kernels' stream); graph replays
+    # carry none.
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+            continue
+        e0, e1 = dom_ev[i]
+        if dominant == "combine":
+            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
+            e0.record(stream)
+            ops.combine(h, y, w, out=out)
+            e1.record(stream)
+        else:
+            h = ops.layout(cfg, idx, w, workspace=ws)
+            e0.record(stream)
+            ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs) if fp8 else ops.dispatch(h, x, dtype, recv=recv)
+            e1.record(stream)
+            ops.combine(h, y, w, out=out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # Per-kernel durations: the same K steps again with HIP events recorded
-    # around each call on the stream the kernels run on (an event marker
-    # leaves a few-microsecond bubble, so this pass is not the timed one).
+    dom_live_ms = None if graph is not None else float(np.mean([a.elapsed_time(b) for a, b in dom_ev]))
+    # Per-kernel durations: K more steps as separate layout / dispatch /
+    # combine calls with events between them (not part of the timed region).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(evs[i])
+        step_split(evs[i])
     torch.cuda.synchronize()
     lay_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dis_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     com_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     gpu_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    # dispatch_forward as one unit (one launch for small batches)
+    fw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in fw:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_ev_ms = float(np.mean([a.elapsed_time(b) for a, b in fw]))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     khash = kernel_hash()
     com_gbps = nbytes["combine"] / (com_ms * 1e-3) / 1e9
     dis_gbps = nbytes["dispatch"] / (dis_ms * 1e-3) / 1e9
-    dominant = "combine" if nbytes["combine"] >= nbytes["dispatch"] else "dispatch"
-    dom_gbps = com_gbps if dominant == "combine" else dis_gbps
+    dom_ms = dom_live_ms if dom_live_ms is not None else (com_ms if dominant == "combine" else dis_ms)
+    dom_gbps = nbytes[dominant] / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic("k_combine" if dominant == "combine" else "k_dispatch", khash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "k_combine<true>" if dominant == "combine" else "k_dispatch",
                 "algorithmic_bytes_per_launch": nbytes[dominant],
-                "avg_launch_us": round((com_ms if dominant == "combine" else dis_ms) * 1e3, 2)}
+                "avg_launch_us": round(dom_ms * 1e3, 2),
+                "timed": "events in the timed region" if dom_live_ms is not None else "evented eager pass"}
 
     copy_ceiling = None
     if not args.no_copy_ceiling:
@@ -239,7 +297,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
+        "config": {"workload": wl.name, "graph": bool(args.graph), "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
                    "expert_alignment": wl.A, "dests": wl.D, "mode": "fixed" if wl.mode else "compact",
                    "dispatch": "fp8_e4m3_1x128" if fp8 else "bf16", "combine": "bf16", "routing": wl.routing},
         "roofline": roofline,
@@ -247,6 +305,7 @@ def main():
         "kernels": {
             "layout_us": round(lay_ms * 1e3, 2), "dispatch_us": round(dis_ms * 1e3, 2),
             "combine_us": round(com_ms * 1e3, 2), "gpu_step_us": round(gpu_ms * 1e3, 2),
+            "dispatch_forward_plus_combine_us": round(step_ev_ms * 1e3, 2), "graph": bool(args.graph),
             "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
             "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
             "bytes": nbytes, "kernel_hash": khash,

@@ -259,6 +259,22 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
 
 }  // namespace
 
+namespace ep {
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace ep
+
 extern "C" {
 
 size_t ep_workspace_bytes(const ep_config* cfg) {

@@ -3,18 +3,19 @@
 // combine without weights that also gathers per-row values back to the
 // pairs), for the receive rows of one GPU.
 //
-// One block per token; each lane owns 8 channels (one dwordx4 of bf16) of
-// the output row. It issues the loads of all k source rows (up to 8 at a
-// time) before any arithmetic, so k 16-byte loads per lane are in flight,
-// then accumulates in binary32 with fused multiply-add in k order from +0,
-// rounds to bf16 (nearest even) and writes one dwordx4.
+// One block per token (or, for batches too small to fill the chip, per piece
+// of seg vectors of a token's row); each lane owns 8 channels (one dwordx4
+// of bf16) of the output row. It issues the loads of all k source rows (up
+// to 8 at a time) before any arithmetic, so k 16-byte loads per lane are in
+// flight, then accumulates in binary32 with fused multiply-add in k order
+// from +0, rounds to bf16 (nearest even) and writes one dwordx4.
 #include "ep_internal.h"
 
 namespace ep {
 
 template <bool WEIGHTED>
 __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
-    const int t = blockIdx.x;
+    const int t = blockIdx.x / a.nsplit, part = blockIdx.x % a.nsplit;
     const int tid = threadIdx.x, lane = tid & 63;
     // Lane j < k of every wave holds pair j's slot and weight; the loops below
     // broadcast them with readlane, so no load sits between the row loads.
@@ -24,11 +25,11 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         my_s = a.slot[(int64_t)t * a.k + lane];
         if (WEIGHTED) my_w = a.w[(int64_t)t * a.k + lane];
     }
-    if (a.out_vals != nullptr && tid < a.k)
+    if (a.out_vals != nullptr && part == 0 && tid < a.k)
         a.out_vals[(int64_t)t * a.k + tid] = my_s >= 0 ? a.row_vals[my_s] : 0.0f;
 
-    const int nvec = a.H / 8;
-    for (int c = tid; c < nvec; c += blockDim.x) {
+    const int c1 = min((part + 1) * a.seg, a.H / 8);
+    for (int c = part * a.seg + tid; c < c1; c += blockDim.x) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -72,16 +73,23 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     }
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-    if (a.T == 0) return hipSuccess;
+hipError_t launch_combine(const CombineArgs& args, hipStream_t stream) {
+    if (args.T == 0) return hipSuccess;
+    CombineArgs a = args;
     const int nvec = a.H / 8;
-    int threads = ((nvec + 63) / 64) * 64;
+    // Batches with fewer tokens than about two per CU split each row into
+    // pieces of at least 64 vectors, so that the gather reaches every CU.
+    int nsplit = (kSplitTargetBlocks + a.T - 1) / a.T;
+    nsplit = max(1, min(nsplit, nvec / 64));
+    a.seg = (nvec + nsplit - 1) / nsplit;
+    a.nsplit = (nvec + a.seg - 1) / a.seg;
+    int threads = ((a.seg + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
-    if (threads < 64) threads = 64;
+    const dim3 grid((unsigned)a.T * a.nsplit);
     if (a.w != nullptr)
-        hipLaunchKernelGGL(k_combine<true>, dim3(a.T), dim3(threads), 0, stream, a);
+        hipLaunchKernelGGL(k_combine<true>, grid, dim3(threads), 0, stream, a);
     else
-        hipLaunchKernelGGL(k_combine<false>, dim3(a.T), dim3(threads), 0, stream, a);
+        hipLaunchKernelGGL(k_combine<false>, grid, dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
         my_s = a.slot[(int64_t)t * a.k + lane];
         if (KIND == kDispatchBf16Weighted) my_w = a.pair_w[(int64_t)t * a.k + lane];
     }
-    dispatch_token<KIND>(a, t, my_s, my_w);
+    dispatch_token<KIND>(a, t, 0, dispatch_nvec<KIND>(a), my_s, my_w);
 }
 
 hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream) {

@@ -57,88 +57,117 @@ __device__ __forceinline__ void dispatch_zero_rows(const DispatchArgs& a, int r0
     }
 }
 
-// Copies token t's row into the receive rows of its k pairs with the whole
-// block. Lane j < k of every wave holds pair j's row in my_s (-1 = skipped)
-// and, for the weighted kind, its weight in my_w; the store loops broadcast
-// them with readlane, so no load waits between stores.
+// What one lane holds of a token's row between the load and the stores.
+// Raw: the loaded bytes (BF16: one 16-byte vector of 8 values; FP8 quantise:
+// two vectors, 16 values; FP8 copy: one vector of 16 codes and its block's
+// scale). Vec: what is stored (the vector, and the 1x128 scale for FP8).
+struct DispatchRaw {
+    uint4 v0, v1;
+    float scale;
+};
+struct DispatchVec {
+    uint4 v;
+    float scale;
+};
+
+// Issues the loads of vector c of token t's row (no arithmetic, so callers
+// can overlap them with other work).
 template <int KIND>
-__device__ __forceinline__ void dispatch_token(const DispatchArgs& a, int t, int my_s, float my_w) {
-    constexpr bool kFp8 = dispatch_is_fp8(KIND);
-    const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int64_t row_out = kFp8 ? (int64_t)a.H : 2 * (int64_t)a.H;
-    const int nb = a.H / 128;
+__device__ __forceinline__ DispatchRaw dispatch_load(const DispatchArgs& a, int t, int c, bool act) {
+    DispatchRaw r;
+    r.v0 = make_uint4(0u, 0u, 0u, 0u);
+    r.v1 = r.v0;
+    r.scale = 0.0f;
+    if (!act) return r;
     if (KIND == kDispatchBf16 || KIND == kDispatchBf16Weighted) {
-        const uint4* src = (const uint4*)((const char*)a.x + (int64_t)t * 2 * a.H);
-        const int nvec = a.H / 8;
-        for (int c = tid; c < nvec; c += nthreads) {
-            const uint4 v = src[c];
-            float f[8];
-            if (KIND == kDispatchBf16Weighted) unpack_bf16x8(v, f);
-            for (int j = 0; j < a.k; ++j) {
-                const int s = __builtin_amdgcn_readlane(my_s, j);
-                if (s < 0) continue;
-                uint4 o = v;
-                if (KIND == kDispatchBf16Weighted) {
-                    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
-                    float g[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) g[i] = wj * f[i];
-                    o = pack_bf16x8(g);
-                }
-                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
-            }
-        }
+        r.v0 = ((const uint4*)((const char*)a.x + (int64_t)t * 2 * a.H))[c];
     } else if (KIND == kDispatchFp8Quant) {
         const uint4* src = (const uint4*)((const char*)a.x + (int64_t)t * 2 * a.H);
-        const int nvec = a.H / 16;  // 16 bf16 in, 16 codes out per lane
-        // The loop bound is uniform so every lane of a wave takes part in the
-        // DPP reduction; `act` only guards memory.
-        for (int c0 = 0; c0 < nvec; c0 += nthreads) {
-            const int c = c0 + tid;
-            const bool act = c < nvec;
-            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
-            if (act) {
-                v0 = src[2 * c];
-                v1 = src[2 * c + 1];
-            }
-            float f[16];
-            unpack_bf16x8(v0, f);
-            unpack_bf16x8(v1, f + 8);
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-            amax = max8_dpp(amax);
-            const float scale = amax / 448.0f;
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            if (amax != 0.0f) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) w4[i >> 2] |= f32_to_e4m3_sat(f[i] / scale) << (8 * (i & 3));
-            }
-            const uint4 o = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-            if (act) {
-                for (int j = 0; j < a.k; ++j) {
-                    const int s = __builtin_amdgcn_readlane(my_s, j);
-                    if (s < 0) continue;
-                    store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
-                    if ((c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = scale;
-                }
-            }
-        }
+        r.v0 = src[2 * c];
+        r.v1 = src[2 * c + 1];
     } else {  // kDispatchFp8Copy
-        const uint4* src = (const uint4*)((const char*)a.x + (int64_t)t * a.H);
-        const int nvec = a.H / 16;
-        for (int c = tid; c < nvec; c += nthreads) {
-            const uint4 v = src[c];
-            const bool scale_lane = (c & 7) == 0;
-            const float sc = scale_lane ? a.x_scales[(int64_t)t * nb + (c >> 3)] : 0.0f;
-            for (int j = 0; j < a.k; ++j) {
-                const int s = __builtin_amdgcn_readlane(my_s, j);
-                if (s < 0) continue;
-                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, v);
-                if (scale_lane) a.recv_scales[(int64_t)s * nb + (c >> 3)] = sc;
-            }
+        r.v0 = ((const uint4*)((const char*)a.x + (int64_t)t * a.H))[c];
+        if ((c & 7) == 0) r.scale = a.x_scales[(int64_t)t * (a.H / 128) + (c >> 3)];
+    }
+    return r;
+}
+
+// Turns loaded bytes into what is stored. FP8 quantise: amax of the 1x128
+// block over eight consecutive lanes (DPP), scale = amax / 448, codes =
+// E4M3(x / scale); every lane of the wave must call it (inactive lanes hold
+// zeros), and vectors must be grouped in aligned runs of eight.
+template <int KIND>
+__device__ __forceinline__ DispatchVec dispatch_encode(const DispatchRaw& r) {
+    DispatchVec d;
+    d.v = r.v0;
+    d.scale = r.scale;
+    if (KIND == kDispatchFp8Quant) {
+        float f[16];
+        unpack_bf16x8(r.v0, f);
+        unpack_bf16x8(r.v1, f + 8);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = max8_dpp(amax);
+        const float scale = amax / 448.0f;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        if (amax != 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w4[i >> 2] |= f32_to_e4m3_sat(f[i] / scale) << (8 * (i & 3));
         }
+        d.v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        d.scale = scale;
+    }
+    return d;
+}
+
+// Stores vector c of a loaded row into the receive rows of the token's k
+// pairs. Lane j < k of every wave holds pair j's row in my_s (-1 = skipped)
+// and, for the weighted kind, its weight in my_w; the loop broadcasts them
+// with readlane, so no load waits between stores.
+template <int KIND>
+__device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const DispatchVec& d, int c, bool act,
+                                               int my_s, float my_w) {
+    constexpr bool kFp8 = dispatch_is_fp8(KIND);
+    const int64_t row_out = kFp8 ? (int64_t)a.H : 2 * (int64_t)a.H;
+    const int nb = a.H / 128;
+    float f[8];
+    if (KIND == kDispatchBf16Weighted) unpack_bf16x8(d.v, f);
+    if (!act) return;
+    for (int j = 0; j < a.k; ++j) {
+        const int s = __builtin_amdgcn_readlane(my_s, j);
+        if (s < 0) continue;
+        uint4 o = d.v;
+        if (KIND == kDispatchBf16Weighted) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+            float g[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = wj * f[i];
+            o = pack_bf16x8(g);
+        }
+        store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
+        if (kFp8 && (c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = d.scale;
+    }
+}
+
+// Vectors per row: 8 bf16 (BF16 kinds) or 16 codes (FP8 kinds) per vector.
+template <int KIND>
+__device__ __forceinline__ int dispatch_nvec(const DispatchArgs& a) {
+    return dispatch_is_fp8(KIND) ? a.H / 16 : a.H / 8;
+}
+
+// Copies vectors [c0, c1) of token t's row into the receive rows of its k
+// pairs with the whole block (c0 a multiple of 8 for the FP8 kinds). The
+// loop bound is uniform across the block, so every lane of a wave takes part
+// in the FP8 amax reduction; `act` only guards memory.
+template <int KIND>
+__device__ __forceinline__ void dispatch_token(const DispatchArgs& a, int t, int c0, int c1, int my_s,
+                                               float my_w) {
+    for (int cb = c0; cb < c1; cb += blockDim.x) {
+        const int c = cb + threadIdx.x;
+        const bool act = c < c1;
+        const DispatchVec d = dispatch_encode<KIND>(dispatch_load<KIND>(a, t, c, act));
+        dispatch_store<KIND>(a, d, c, act, my_s, my_w);
     }
 }
 

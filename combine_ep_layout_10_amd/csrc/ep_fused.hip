@@ -6,11 +6,17 @@
 // The layout has a grid-wide dependency (a token's row depends on the
 // counts of every expert before it), so instead of waiting on other blocks
 // every block recomputes the whole layout of the batch in LDS (pairs <=
-// 4096, E <= 512: a few KiB of ids read from L2 per block). Block 0 writes
-// the handle's arrays; the next blocks zero-fill padding rows; the rest copy
-// one token each, taking their slots from the lanes that ranked their pairs.
-// No block waits on another, and the result equals ep_layout followed by
-// ep_dispatch bit for bit (the same device code computes both).
+// 4096, E <= 512: a few KiB of ids read from L2 per block). The first
+// blocks copy one piece (seg vectors) of one token's row each, taking the
+// token's slots from the lanes that ranked its pairs; the last ones
+// zero-fill padding rows; block 0 also writes the handle's arrays. A token
+// block issues the loads of its piece of x before the layout work, so both
+// round trips overlap. Small batches have few tokens, so rows are split over
+// several blocks to reach every CU, but the grid is kept to one block per CU:
+// a block left for a second round would double the time, and two blocks on
+// one CU slow each other's layout work. No block waits on another, and the
+// result equals ep_layout followed by ep_dispatch bit for bit (the same
+// device code computes both).
 #include "ep_internal.h"
 #include "ep_layout_dev.h"
 #include "ep_dispatch_dev.h"
@@ -21,23 +27,30 @@ template <int IT, int KIND>
 __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, DispatchArgs da) {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_slot[kMaxTopk];
+    const int ntok = da.T * da.nsplit;                  // token-piece blocks come first
+    const bool tok = (int)blockIdx.x < ntok;
+    const int t = tok ? (int)blockIdx.x / da.nsplit : 0;
+    const int part = tok ? (int)blockIdx.x % da.nsplit : 0;
+    const int c = part * da.seg + (int)threadIdx.x;
+    const int c_end = min((part + 1) * da.seg, dispatch_nvec<KIND>(da));
+    const bool act = tok && (int)threadIdx.x < da.seg && c < c_end;
+    const DispatchRaw raw = dispatch_load<KIND>(da, t, c, act);
+
     SmallLayout<IT> L;
     const bool lead = blockIdx.x == 0;
     small_layout<IT>(la, lds, lead, L);
-    if (lead) {
-        small_layout_publish<IT>(la, L);
-        return;
-    }
-    const int b = (int)blockIdx.x - 1;
-    if (b < da.npad_blocks) {
-        const int e = b / da.pad_blocks_per_expert;
-        const int part = b % da.pad_blocks_per_expert;
-        const int r0 = L.s_off[e] + L.s_cnt[e] + part * kPadRowsPerBlock;
+    if (lead) small_layout_publish<IT>(la, L);
+    if (!tok) {
+        if (lead && ntok == 0 && da.npad_blocks == 0) return;  // an empty batch: the handle only
+        const int pb = (int)blockIdx.x - ntok;
+        if (pb >= da.npad_blocks) return;
+        const int e = pb / da.pad_blocks_per_expert;
+        const int pp = pb % da.pad_blocks_per_expert;
+        const int r0 = L.s_off[e] + L.s_cnt[e] + pp * kPadRowsPerBlock;
         const int r1 = min(r0 + kPadRowsPerBlock, L.s_off[e + 1]);
         dispatch_zero_rows<KIND>(da, r0, r1);
         return;
     }
-    const int t = b - da.npad_blocks;
     const int lane = threadIdx.x & 63;
     const int64_t p0 = (int64_t)t * la.k;
 #pragma unroll
@@ -46,8 +59,10 @@ __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, D
         if (p >= p0 && p < p0 + la.k) s_slot[p - p0] = small_layout_slot<IT>(la, L, it);
     }
     __syncthreads();
+    if ((int)threadIdx.x >= ((da.seg + 63) & ~63)) return;  // whole waves past the piece
     const int my_s = lane < la.k ? s_slot[lane] : -1;
-    dispatch_token<KIND>(da, t, my_s, 0.0f);
+    const DispatchVec d = dispatch_encode<KIND>(raw);
+    dispatch_store<KIND>(da, d, c, act, my_s, 0.0f);
 }
 
 template <int KIND>
@@ -60,8 +75,25 @@ static void launch_fused_kind(const LayoutArgs& la, const DispatchArgs& da, int 
 
 bool fused_layout_dispatch_fits(int64_t pairs, int E) { return pairs <= kSmallMaxPairs && E <= kSmallMaxExperts; }
 
-hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, hipStream_t stream) {
-    const int grid = 1 + da.npad_blocks + da.T;
+hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& args,
+                                        hipStream_t stream) {
+    DispatchArgs da = args;
+    const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy;
+    const int nvec = fp8 ? da.H / 16 : da.H / 8;
+    // Pieces per row: as many as keep the grid within kFusedBlocksPerCU
+    // blocks per CU (padding blocks included), at least 64 vectors per
+    // piece, at most 1024 (one vector per thread).
+    const int resident = kFusedBlocksPerCU * device_cu_count();
+    int nsplit = da.T > 0 ? max(1, (resident - da.npad_blocks) / da.T) : 1;
+    nsplit = min(nsplit, (nvec + 63) / 64);
+    nsplit = max(nsplit, (nvec + 1023) / 1024);
+    nsplit = max(nsplit, 1);
+    int seg = (nvec + nsplit - 1) / nsplit;
+    seg = (seg + 7) & ~7;
+    da.seg = seg;
+    da.nsplit = (nvec + seg - 1) / seg;
+    int grid = da.T * da.nsplit + da.npad_blocks;
+    if (grid == 0) grid = 1;  // the handle of an empty batch is still written
     const size_t lds = small_layout_lds_bytes(la.E, la.D);
     switch (kind) {
         case kDispatchBf16: launch_fused_kind<kDispatchBf16>(la, da, grid, lds, stream); break;

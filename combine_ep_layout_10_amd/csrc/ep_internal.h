@@ -61,6 +61,9 @@ struct DispatchArgs {
     int zero_pad;
     int pad_blocks_per_expert;
     int npad_blocks;
+    // single-launch layout + dispatch only: each token's row is split into
+    // nsplit blocks of seg vectors (seg <= 1024, a multiple of 8)
+    int nsplit, seg;
 };
 
 struct CombineArgs {
@@ -71,7 +74,19 @@ struct CombineArgs {
     const float* row_vals;
     float* out_vals;
     int T, H, k;
+    int nsplit, seg;  // each token's row is split into nsplit blocks of seg vectors
 };
+
+// Combine splits the rows of batches smaller than this many tokens so that
+// about this many blocks gather.
+constexpr int kSplitTargetBlocks = 512;
+// Blocks of the single-launch layout + dispatch per CU. Every block redoes
+// the small layout, so a second block on a CU competes with the first for
+// its SIMDs (measured on MI355X at 128 x 7168 x top-8: one block per CU,
+// two pieces per row, beats two blocks per CU by about 4 us).
+constexpr int kFusedBlocksPerCU = 1;
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 
 // Rows of padding one dispatch block clears.
 constexpr int kPadRowsPerBlock = 16;
