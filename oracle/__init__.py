@@ -63,6 +63,8 @@ def _load():
     lib.ora_dispatch_fp8_prequant.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, i32, P, P]
     lib.ora_combine.restype = None
     lib.ora_combine.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.ora_combine_weight_grad.restype = None
+    lib.ora_combine_weight_grad.argtypes = [i32, i32, i32, P, P, P, P]
     lib.ora_e4m3_encode_many.restype = None
     lib.ora_e4m3_encode_many.argtypes = [P, ctypes.c_int64, P]
     lib.ora_bf16_rne_many.restype = None
@@ -217,6 +219,21 @@ def combine_backward_bf16(lay: dict, grad_out: np.ndarray, k: int,
     """README combine_backward: a dispatch on the same layout; with weights,
     each copy is scaled by its pair weight (gradient of a weighted combine)."""
     return dispatch_bf16(lay, grad_out, k, pair_w=topk_w, zero_pad=zero_pad)
+
+
+def combine_weight_grad(lay: dict, grad_out: np.ndarray, y: np.ndarray, k: int) -> np.ndarray:
+    """Gradient of the weighted combine with respect to topk_w: [T, k]
+    float64, grad_w[t, j] = sum_h grad_out[t, h] * y[slot[t, j], h] (0 for
+    skipped pairs), exact products summed in binary64 in channel order."""
+    lib = _load()
+    g = _c(grad_out, np.uint16)
+    y = _c(y, np.uint16)
+    T, H = g.shape
+    if y.shape[1] != H or lay["slot"].shape[0] != T * k:
+        raise ValueError("grad_out [T, H], y [rows, H] and the layout must agree")
+    out = np.empty((T, k), np.float64)
+    lib.ora_combine_weight_grad(T, H, k, _p(g), _p(y), _p(lay["slot"]), _p(out))
+    return out
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:

@@ -21,7 +21,9 @@
  *     and BF16 combine for the 8K x 7168 x top-8 setting.
  *   - Backward duals: dispatch_backward is a combine that also returns the
  *     combined weight gradients, combine_backward is a dispatch on the handle
- *     (same section, dispatch_backward / combine_backward).
+ *     (same section, dispatch_backward / combine_backward); the weighted
+ *     combine's gradient with respect to its weights is one dot product per
+ *     (token, k) pair.
  *   - A fixed per-expert receive capacity for decode: "Example use in
  *     inference decoding" (num_max_tokens_per_rank, cached handle).
  * The pages give no kernel internals, rounding rules or FP8 recipe. Where
@@ -401,6 +403,35 @@ void ora_combine(int T, int H, int k, const uint16_t* y, const int32_t* slot,
                 int32_t s = slot[(int64_t)t * k + j];
                 out_vals[(int64_t)t * k + j] = s < 0 ? 0.0f : row_vals[s];
             }
+        }
+    }
+}
+
+/* Gradient of the weighted combine with respect to its weights. The
+ * combine above computes out[t] = sum_j w[t, j] * y[slot[t, j]] (README
+ * combine_forward, weighted; its backward, README combine_backward, is a
+ * dispatch of grad_out for the expert outputs). For a loss whose gradient
+ * with respect to out[t] is g[t], the gradient with respect to w[t, j] is
+ * therefore sum_h g[t, h] * y[slot[t, j], h]: the dot product of the token's
+ * output gradient with the expert-output row of pair (t, j). Masked and
+ * overflowed pairs (slot -1) take no part in the combine and get 0.
+ * Computed in binary64: every product of two bfloat16 values is exact in
+ * binary64 (8 + 8 significand bits), and the H products are added in order
+ * h = 0..H-1. */
+void ora_combine_weight_grad(int T, int H, int k, const uint16_t* grad_out, const uint16_t* y,
+                             const int32_t* slot, double* grad_w) {
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t s = slot[(int64_t)t * k + j];
+            double acc = 0.0;
+            if (s >= 0) {
+                for (int h = 0; h < H; ++h) {
+                    double g = (double)ora_bf16_value(grad_out[(int64_t)t * H + h]);
+                    double v = (double)ora_bf16_value(y[(int64_t)s * H + h]);
+                    acc += g * v;
+                }
+            }
+            grad_w[(int64_t)t * k + j] = acc;
         }
     }
 }

@@ -427,3 +427,62 @@ def test_combine_masked_pairs_and_fp8_identity():
         else:
             assert np.all(out1[t] == 0)
     assert yq.shape == (R, H)
+
+
+# ---------------------------------------------------------------- combine weight gradient
+
+def test_weight_grad_exact_integers():
+    """Integer-valued bf16 gradients and expert outputs: every product and
+    partial sum is an exact small integer, so the oracle must equal the dot
+    product taken with Python integers over the row that holds each pair,
+    found by brute force (the row whose row_src is the pair index)."""
+    rng = np.random.default_rng(31)
+    for T, E, k, A, H, masked in [(9, 5, 2, 3, 40, 0.0), (30, 8, 3, 1, 64, 0.2), (17, 4, 4, 2, 8, 0.1)]:
+        idx = random_routing_table(rng, T, E, k, masked_frac=masked, distinct=False)
+        lay = oracle.layout(0, T, E, k, A, 1, 0, idx)
+        R = lay["rows_bound"]
+        gi = rng.integers(-16, 17, size=(T, H))
+        yi = rng.integers(-16, 17, size=(R, H))
+        g = f32_to_bf16_bits(gi.astype(np.float32))
+        y = f32_to_bf16_bits(yi.astype(np.float32))
+        got = oracle.combine_weight_grad(lay, g, y, k)
+        for t in range(T):
+            for j in range(k):
+                rows = [r for r in range(lay["rows"]) if lay["row_src"][r] == t * k + j]
+                assert len(rows) == (1 if idx[t, j] >= 0 else 0)
+                want = sum(int(a) * int(b) for a, b in zip(gi[t], yi[rows[0]])) if rows else 0
+                assert got[t, j] == want, (t, j)
+
+
+def test_weight_grad_closed_forms():
+    """Constant rows give H * a * b exactly; pairs past a FIXED capacity get 0;
+    with expert outputs equal to the dispatched x (identity experts) every
+    pair of token t gets <g_t, x_t>, checked against math.fsum of the exact
+    binary64 products within the binary64 bound of an H-term sum."""
+    import math
+    T, E, k, H = 12, 4, 2, 384
+    rng = np.random.default_rng(32)
+    idx = random_routing_table(rng, T, E, k)
+    lay = oracle.layout(0, T, E, k, 1, 1, 0, idx)
+    g = np.full((T, H), f32_to_bf16_bits(np.array([0.75], np.float32))[0], np.uint16)
+    y = np.full((lay["rows_bound"], H), f32_to_bf16_bits(np.array([-1.5], np.float32))[0], np.uint16)
+    assert np.all(oracle.combine_weight_grad(lay, g, y, k) == H * 0.75 * -1.5)
+    # FIXED capacity 2: the pairs past it are skipped and get 0
+    idx_f = np.zeros((T, k), np.int64)
+    idx_f[:, 1] = 1
+    lay_f = oracle.layout(1, T, E, k, 1, 1, 2, idx_f)
+    y_f = np.full((lay_f["rows_bound"], H), y[0, 0], np.uint16)
+    got = oracle.combine_weight_grad(lay_f, g, y_f, k)
+    assert np.all(got[:2] == H * 0.75 * -1.5) and np.all(got[2:] == 0.0)
+    # identity experts
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    gr = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    recv = oracle.dispatch_bf16(lay, x, k)
+    got = oracle.combine_weight_grad(lay, gr, recv, k)
+    x64 = bf16_bits_to_f32(x).astype(np.float64)
+    g64 = bf16_bits_to_f32(gr).astype(np.float64)
+    for t in range(T):
+        terms = [a * b for a, b in zip(g64[t], x64[t])]
+        exact = math.fsum(terms)
+        bound = H * 2.0 ** -53 * math.fsum(abs(v) for v in terms)
+        assert np.all(np.abs(got[t] - exact) <= bound)
