@@ -83,6 +83,7 @@ _SIGNATURES = {
     "ep_combine": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),
     "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int, _P, _P, _P, _P, _P]),
+    "ep_combine_weight_grad": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_handle_check": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P]),
     "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -164,6 +165,11 @@ def ep_combine_backward(h: ep_handle, dtype: int, grad_out: int, topk_w, grad_y:
                         stream: int) -> None:
     _check(lib().ep_combine_backward(ctypes.byref(h), int(dtype), grad_out, topk_w, grad_y, grad_y_scales,
                                      stream), "ep_combine_backward")
+
+
+def ep_combine_weight_grad(h: ep_handle, grad_out: int, y: int, grad_topk_w: int, stream: int) -> None:
+    _check(lib().ep_combine_weight_grad(ctypes.byref(h), grad_out, y, grad_topk_w, stream),
+           "ep_combine_weight_grad")
 
 
 def ep_handle_read_counts(h: ep_handle, cnt, pad, rows, stream: int) -> None:

@@ -357,6 +357,30 @@ ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* gr
     return do_dispatch(h, dtype, grad_out, nullptr, topk_w, grad_y, grad_y_scales, (hipStream_t)stream);
 }
 
+ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const void* y, float* grad_topk_w,
+                                 void* stream) {
+    ep_status s = check_handle(h);
+    if (s != EP_OK) return s;
+    const int T = h->num_tokens;
+    if (T > 0 && (grad_out == nullptr || !aligned(grad_out, 16)))
+        return fail(EP_ERR_INVALID_ARG, "grad_out must be non-NULL and 16-byte aligned");
+    if (T > 0 && (y == nullptr || !aligned(y, 16)))
+        return fail(EP_ERR_INVALID_ARG, "y must be non-NULL and 16-byte aligned");
+    if (T > 0 && (grad_topk_w == nullptr || !aligned(grad_topk_w, 4)))
+        return fail(EP_ERR_INVALID_ARG, "grad_topk_w must be non-NULL and 4-byte aligned");
+    ep::WeightGradArgs a;
+    a.grad_out = (const uint16_t*)grad_out;
+    a.y = (const uint16_t*)y;
+    a.slot = h->slot;
+    a.grad_w = grad_topk_w;
+    a.T = T;
+    a.H = h->cfg.hidden;
+    a.k = h->cfg.num_topk;
+    hipError_t e = ep::launch_weight_grad(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "weight gradient launch");
+    return EP_OK;
+}
+
 ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, int64_t* rows, void* stream) {
     ep_status s = check_handle(h);
     if (s != EP_OK) return s;

@@ -73,6 +73,86 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     }
 }
 
+// Gradient of the weighted combine with respect to its weights: for every
+// pair, grad_w[t, j] = sum_c grad_out[t, c] * y[slot[t, j], c], the dot
+// product of the token's output gradient with the pair's expert-output row
+// (0 for skipped pairs). One block per token, each lane owning 8 channels
+// per vector as in the combine: the lane loads its grad_out vector once and
+// the k row vectors (all issued before the arithmetic), accumulates one
+// binary32 partial per pair with fused multiply-adds over its channels, in
+// channel order and then over its vectors in order; the 64 lanes of a wave
+// are summed by a butterfly (xor 32, 16, ..., 1), and the waves' sums are
+// added by thread j in wave order. The order is fixed, so the result is
+// deterministic; a product passes through at most
+// 8 * ceil(vectors / threads) + 6 + waves - 1 binary32 additions.
+__global__ __launch_bounds__(1024) void k_weight_grad(WeightGradArgs a) {
+    __shared__ float red[16][kMaxTopk];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int my_s = -1;
+    if (lane < a.k) my_s = a.slot[(int64_t)t * a.k + lane];
+    const int nvec = a.H / 8;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+        for (int c = tid; c < nvec; c += blockDim.x) {
+            const uint4 gv = ((const uint4*)(a.grad_out + (int64_t)t * a.H))[c];
+            uint4 v[8];
+            int s[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s[u] = j0 + u < a.k ? __builtin_amdgcn_readlane(my_s, j0 + u) : -1;
+                v[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (s[u] >= 0) v[u] = load_stream((const uint4*)(a.y + (int64_t)s[u] * a.H) + c);
+            }
+            float g[8];
+            g[0] = bf16_to_f32(gv.x & 0xFFFFu);
+            g[1] = bf16_to_f32(gv.x >> 16);
+            g[2] = bf16_to_f32(gv.y & 0xFFFFu);
+            g[3] = bf16_to_f32(gv.y >> 16);
+            g[4] = bf16_to_f32(gv.z & 0xFFFFu);
+            g[5] = bf16_to_f32(gv.z >> 16);
+            g[6] = bf16_to_f32(gv.w & 0xFFFFu);
+            g[7] = bf16_to_f32(gv.w >> 16);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc[u] = __builtin_fmaf(g[0], bf16_to_f32(v[u].x & 0xFFFFu), acc[u]);
+                acc[u] = __builtin_fmaf(g[1], bf16_to_f32(v[u].x >> 16), acc[u]);
+                acc[u] = __builtin_fmaf(g[2], bf16_to_f32(v[u].y & 0xFFFFu), acc[u]);
+                acc[u] = __builtin_fmaf(g[3], bf16_to_f32(v[u].y >> 16), acc[u]);
+                acc[u] = __builtin_fmaf(g[4], bf16_to_f32(v[u].z & 0xFFFFu), acc[u]);
+                acc[u] = __builtin_fmaf(g[5], bf16_to_f32(v[u].z >> 16), acc[u]);
+                acc[u] = __builtin_fmaf(g[6], bf16_to_f32(v[u].w & 0xFFFFu), acc[u]);
+                acc[u] = __builtin_fmaf(g[7], bf16_to_f32(v[u].w >> 16), acc[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) acc[u] += __shfl_xor(acc[u], off, kWave);
+            if (lane == 0 && j0 + u < a.k) red[w][j0 + u] = acc[u];
+        }
+    }
+    __syncthreads();
+    if (tid < a.k) {
+        const int nw = (blockDim.x + 63) >> 6;
+        float sum = red[0][tid];
+        for (int ww = 1; ww < nw; ++ww) sum += red[ww][tid];
+        const int s = a.slot[(int64_t)t * a.k + tid];
+        a.grad_w[(int64_t)t * a.k + tid] = s >= 0 ? sum : 0.0f;
+    }
+}
+
+hipError_t launch_weight_grad(const WeightGradArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int nvec = a.H / 8;
+    int threads = ((nvec + 63) / 64) * 64;
+    if (threads > 1024) threads = 1024;
+    hipLaunchKernelGGL(k_weight_grad, dim3(a.T), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& args, hipStream_t stream) {
     if (args.T == 0) return hipSuccess;
     CombineArgs a = args;

@@ -88,12 +88,21 @@ constexpr int kFusedBlocksPerCU = 1;
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 
+struct WeightGradArgs {
+    const uint16_t* grad_out;
+    const uint16_t* y;
+    const int32_t* slot;
+    float* grad_w;
+    int T, H, k;
+};
+
 // Rows of padding one dispatch block clears.
 constexpr int kPadRowsPerBlock = 16;
 
 hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
 hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_weight_grad(const WeightGradArgs& a, hipStream_t stream);
 // Single-launch layout + dispatch (unweighted kinds) for small batches.
 bool fused_layout_dispatch_fits(int64_t pairs, int E);
 hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, hipStream_t stream);

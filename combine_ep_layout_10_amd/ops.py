@@ -9,6 +9,7 @@ Mapping to the DeepEP README ("Interfaces and examples"):
   combine                      -> combine_forward
   dispatch_backward            -> dispatch_backward (a combine)
   combine_backward             -> combine_backward (a dispatch on the handle)
+  combine_weight_grad          -> the weight gradient of the weighted combine
   dispatch with an old Handle  -> decode_dispatch with cached_handle
 """
 from __future__ import annotations
@@ -295,3 +296,18 @@ def combine_backward(h: Handle, grad_out: torch.Tensor, dtype: int = BF16, topk_
                           _opt(topk_w, "topk_w", torch.float32), _dev(grad_y, "grad_y", torch.uint8 if dtype != BF16 else torch.bfloat16),
                           _opt(grad_y_scales, "grad_y_scales", torch.float32), _stream())
     return (grad_y, grad_y_scales) if dtype != BF16 else grad_y
+
+
+def combine_weight_grad(h: Handle, grad_out: torch.Tensor, y: torch.Tensor,
+                        grad_topk_w: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the weighted combine with respect to topk_w: [T, k] float32,
+    grad_topk_w[t, j] = <grad_out[t], y[slot[t, j]]> (0 for skipped pairs)."""
+    T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
+    _need(grad_out, (T, H), "grad_out")
+    _need(y, (h.cfg.recv_rows_bound(), H), "y")
+    if grad_topk_w is None:
+        grad_topk_w = torch.empty((T, k), dtype=torch.float32, device=grad_out.device)
+    _need(grad_topk_w, (T, k), "grad_topk_w")
+    F.ep_combine_weight_grad(h.c, _dev(grad_out, "grad_out", torch.bfloat16), _dev(y, "y", torch.bfloat16),
+                             _dev(grad_topk_w, "grad_topk_w", torch.float32), _stream())
+    return grad_topk_w

@@ -227,6 +227,24 @@ ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* gr
                               const float* topk_w, void* grad_y, float* grad_y_scales,
                               void* stream);
 
+/* Gradient of the weighted combine with respect to its weights (the part of
+ * README combine_backward that a weighted combine adds; the gradient with
+ * respect to the expert outputs is ep_combine_backward with topk_w):
+ *   grad_topk_w[t, j] = sum_c float(grad_out[t, c]) * float(y[slot[t, j], c])
+ * in binary32, 0 for skipped pairs.
+ *   grad_out     device bf16 [T, hidden] (gradient of combine's out).
+ *   y            device bf16 [rows bound, hidden]: the expert outputs the
+ *                forward combine read.
+ *   grad_topk_w  device binary32 [T, k].
+ * The sum is taken in a fixed order (per lane over its channels, then a
+ * butterfly over the 64 lanes of a wave, then over the waves in order), so
+ * results are deterministic; each product passes through at most
+ * 8 * ceil((hidden / 8) / 1024) + 6 + 15 binary32 additions, which bounds
+ * the error against the exact sum by that count times 2^-24 times
+ * sum_c |grad_out[t, c] * y[slot, c]|. */
+ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const void* y,
+                                 float* grad_topk_w, void* stream);
+
 /* Copies cnt and pad (host arrays of E, either may be NULL) and the row
  * total R (host, may be NULL) to the host. Synchronises the stream: this is
  * the README's "CPU sync" of a non-cached dispatch. */

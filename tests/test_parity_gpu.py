@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from ep_workloads import WORKLOADS, make_inputs, random_routing_table, f32_to_bf16_bits
+from ep_workloads import WORKLOADS, make_inputs, random_routing_table, f32_to_bf16_bits, bf16_bits_to_f32
 from gpu_common import (log, to_dev, to_dev_bf16, bf16_host, host, cfg_of, workload_case, written_rows,
                         bf16_ulp_distance, compare_layout)
 
@@ -295,6 +295,67 @@ def test_backward_duals():
     assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
     with pytest.raises(Exception):
         ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE, to_dev(w))
+
+
+def _weight_grad_bound(H, g, y, slot):
+    """Error bound of the GPU sum: each product passes through at most
+    d = 8 * ceil(vectors / threads) + 6 + (waves - 1) binary32 additions
+    (lane, wave butterfly, waves in order), so |got - exact| <=
+    gamma_d * sum |g * y| with gamma_d = d u / (1 - d u), u = 2^-24."""
+    nvec = H // 8
+    threads = min(1024, -(-nvec // 64) * 64)
+    d = 8 * -(-nvec // threads) + 6 + (threads // 64 - 1)
+    u = 2.0 ** -24
+    T, k = slot.shape
+    mag = np.empty((T, k))
+    ga = np.abs(g)
+    for j in range(k):
+        mag[:, j] = (ga * np.abs(y[np.maximum(slot[:, j], 0)])).sum(-1)
+    return d * u / (1 - d * u) * mag
+
+
+def _check_weight_grad(h, lay, g_bits, y_bits, k):
+    ref = oracle.combine_weight_grad(lay, g_bits, y_bits, k)
+    got = ops.combine_weight_grad(h, to_dev_bf16(g_bits), to_dev_bf16(y_bits))
+    got2 = ops.combine_weight_grad(h, to_dev_bf16(g_bits), to_dev_bf16(y_bits))
+    got, got2 = host(got).astype(np.float64), host(got2)
+    assert np.array_equal(got.astype(np.float32).view(np.uint32), got2.view(np.uint32))   # deterministic
+    T, H = g_bits.shape
+    slot = lay["slot"].reshape(T, k)
+    bound = _weight_grad_bound(H, bf16_bits_to_f32(g_bits).astype(np.float64), bf16_bits_to_f32(y_bits), slot)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float((err / np.maximum(bound, 1e-300)).max())
+    assert np.all(got[slot < 0] == 0.0)
+    return err, bound
+
+
+@pytest.mark.parametrize("T,H,E,k,A,masked", [
+    (1, 8, 4, 1, 1, 0.0), (77, 264, 12, 3, 4, 0.2), (300, 2048, 32, 8, 16, 0.05),
+    (64, 16384, 16, 6, 1, 0.0),      # two vectors per lane
+    (40, 1024, 8, 12, 2, 0.1),       # k > 8: two groups of pairs
+])
+def test_combine_weight_grad(T, H, E, k, A, masked):
+    log("weight grad T=%d H=%d E=%d k=%d" % (T, H, E, k))
+    rng = np.random.default_rng(T + H)
+    idx = random_routing_table(rng, T, E, k, masked_frac=masked, distinct=masked == 0.0)
+    lay = oracle.layout(0, T, E, k, A, 1, 0, idx)
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A)
+    h = ops.layout(cfg, to_dev(idx))
+    R = cfg.recv_rows_bound()
+    g = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    y = f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    _check_weight_grad(h, lay, g, y, k)
+
+
+def test_combine_weight_grad_v3_full_size():
+    """The 8192 x 7168 x top-8 shape: every pair within the bound."""
+    case = workload_case("v3")
+    wl, inp, lay = case["wl"], case["inp"], case["lay"]
+    h = ops.layout(cfg_of(wl), to_dev(inp["topk_idx"]), to_dev(inp["topk_w"]))
+    rng = np.random.default_rng(41)
+    g = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
+    err, bound = _check_weight_grad(h, lay, g, inp["y"], wl.k)
+    log("v3 weight grad: max err/bound %.3g" % float((err / bound).max()))
 
 
 def test_fp8_prequant_passthrough():
