@@ -63,6 +63,8 @@ def _load():
     lib.ora_dispatch_fp8_prequant.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, i32, P, P]
     lib.ora_combine.restype = None
     lib.ora_combine.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.ora_combine_backward_fp8.restype = None
+    lib.ora_combine_backward_fp8.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, i32, P, P]
     lib.ora_combine_weight_grad.restype = None
     lib.ora_combine_weight_grad.argtypes = [i32, i32, i32, P, P, P, P]
     lib.ora_e4m3_encode_many.restype = None
@@ -234,6 +236,25 @@ def combine_weight_grad(lay: dict, grad_out: np.ndarray, y: np.ndarray, k: int) 
     out = np.empty((T, k), np.float64)
     lib.ora_combine_weight_grad(T, H, k, _p(g), _p(y), _p(lay["slot"]), _p(out))
     return out
+
+
+def combine_backward_fp8(lay: dict, grad_out: np.ndarray, k: int, topk_w: np.ndarray, zero_pad: bool = True):
+    """Weighted combine_backward with FP8 output: each pair's row is
+    bf16_rne(w * g) quantised per 1x128 block (its own scales). Returns
+    (codes [R, H] u8, scales [R, H/128] f32); rows not written keep 0xFF / NaN."""
+    lib = _load()
+    g = _c(grad_out, np.uint16)
+    T, H = g.shape
+    if H % 128:
+        raise ValueError("FP8 needs hidden % 128 == 0")
+    w = _c(topk_w, np.float32)
+    E = lay["cnt"].shape[0]
+    R = lay["rows_bound"]
+    recv = np.full((R, H), 0xFF, np.uint8)
+    scales = np.full((R, H // 128), np.nan, np.float32)
+    lib.ora_combine_backward_fp8(T, H, k, E, _p(g), _p(w), _p(lay["slot"]), _p(lay["cnt"]), _p(lay["pad"]),
+                                 _p(lay["expert_off"]), int(bool(zero_pad)), _p(recv), _p(scales))
+    return recv, scales
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:

@@ -344,6 +344,43 @@ void ora_dispatch_fp8(int T, int H, int k, int E, const uint16_t* x, const int32
     }
 }
 
+/* combine_backward of a weighted combine with FP8 output (README
+ * combine_backward: a dispatch of the output gradient on the handle; the
+ * gradient may travel as FP8). Reading taken here: the copy for pair (t, j)
+ * is the BF16 weighted copy, bf16_rne(w[t, j] * float(g[t, h])), quantised
+ * per 1x128 block exactly as the FP8 dispatch quantises x; each pair has its
+ * own scales since each has its own weight. Padding rows get code 0x00 and
+ * scale 0 when zero_pad is set. */
+void ora_combine_backward_fp8(int T, int H, int k, int E, const uint16_t* g, const float* pair_w,
+                              const int32_t* slot, const int32_t* cnt, const int32_t* pad,
+                              const int32_t* expert_off, int zero_pad, uint8_t* recv, float* recv_scales) {
+    int nb = H / 128;
+    uint16_t row[128];
+    uint8_t q[128];
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[(int64_t)t * k + j];
+            if (r < 0)
+                continue;
+            float w = pair_w[(int64_t)t * k + j];
+            for (int b = 0; b < nb; ++b) {
+                for (int i = 0; i < 128; ++i)
+                    row[i] = ora_bf16_rne(w * ora_bf16_value(g[(int64_t)t * H + (int64_t)b * 128 + i]));
+                recv_scales[(int64_t)r * nb + b] = ora_quantize_block(row, 128, q);
+                memcpy(recv + (int64_t)r * H + (int64_t)b * 128, q, 128);
+            }
+        }
+    }
+    if (zero_pad) {
+        for (int e = 0; e < E; ++e)
+            for (int32_t r = ora_pad_begin(cnt, expert_off, e); r < expert_off[e] + pad[e]; ++r) {
+                memset(recv + (int64_t)r * H, 0, (size_t)H);
+                for (int b = 0; b < nb; ++b)
+                    recv_scales[(int64_t)r * nb + b] = 0.0f;
+            }
+    }
+}
+
 /* FP8 dispatch of an already quantised input (README: x given as the tuple
  * (data, scale_factors)): codes and scales copied bitwise to every slot. */
 void ora_dispatch_fp8_prequant(int T, int H, int k, int E, const uint8_t* xq, const float* xs,

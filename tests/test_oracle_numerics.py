@@ -486,3 +486,49 @@ def test_weight_grad_closed_forms():
         exact = math.fsum(terms)
         bound = H * 2.0 ** -53 * math.fsum(abs(v) for v in terms)
         assert np.all(np.abs(got[t] - exact) <= bound)
+
+
+def test_combine_backward_fp8_weighted():
+    """Weighted FP8 combine_backward: per pair, the codes dequantise to the
+    weighted BF16 gradient within the E4M3 bound (checked in binary64 against
+    w * g computed from torch's bf16 cast, not the oracle's); the block's
+    largest element maps to 448 (0x7E); a zero weight gives zero codes and
+    scale 0; pairs of one token with different weights get different scales;
+    padding rows are zero."""
+    rng = np.random.default_rng(33)
+    T, E, k, A, H = 40, 6, 3, 8, 256
+    idx = random_routing_table(rng, T, E, k)
+    w = rng.random((T, k)).astype(np.float32) + 0.25
+    w[0, 1] = 0.0
+    g = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lay = oracle.layout(0, T, E, k, A, 1, 0, idx, w)
+    q, s = oracle.combine_backward_fp8(lay, g, k, w)
+    vals = torch_e4m3_values()
+    g32 = torch.from_numpy(bf16_bits_to_f32(g))
+    for t in range(T):
+        for j in range(k):
+            r = lay["slot"][t * k + j]
+            ref = (g32[t] * float(w[t, j])).to(torch.bfloat16).to(torch.float64).numpy()   # bf16(w * g)
+            codes = q[r]
+            deq = vals[codes & 0x7F] * np.where(codes & 0x80, -1.0, 1.0)
+            deq = (deq.reshape(-1, 128) * s[r][:, None].astype(np.float64)).ravel()
+            blocks = np.abs(ref).reshape(-1, 128)
+            scale = blocks.max(1) / 448.0
+            err = np.abs(deq - ref).reshape(-1, 128)
+            lim = np.maximum(2.0 ** -4 * np.abs(ref).reshape(-1, 128), 2.0 ** -10 * scale[:, None]) * (1 + 2.0 ** -20)
+            assert np.all(err <= lim), (t, j)
+            # exact: the pinned block quantiser applied to torch's bf16(w * g)
+            ref_bits = f32_to_bf16_bits(ref.astype(np.float32))
+            for b in range(H // 128):
+                sc, qb = oracle.quantize_block(ref_bits[b * 128:(b + 1) * 128])
+                assert np.array_equal(codes[b * 128:(b + 1) * 128], qb) and s[r][b] == sc, (t, j, b)
+            if w[t, j] == 0.0:
+                assert np.all(codes == 0) and np.all(s[r] == 0.0)
+            else:
+                assert np.all(np.any((codes.reshape(-1, 128) & 0x7F) == 0x7E, axis=1))
+    t = 5
+    rows = lay["slot"][t * k: t * k + k]
+    assert len({float(s[r][0]) for r in rows}) == k
+    R = lay["rows"]
+    pad_rows = [r for r in range(R) if lay["row_src"][r] < 0]
+    assert pad_rows and np.all(q[pad_rows] == 0) and np.all(s[pad_rows] == 0.0)
