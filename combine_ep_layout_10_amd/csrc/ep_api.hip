@@ -116,8 +116,8 @@ ep_status prepare_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, co
     const bool fp8 = dtype != EP_BF16;
     if (fp8 && c.hidden % 128 != 0)
         return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)", c.hidden);
-    if (pair_w != nullptr && dtype != EP_BF16)
-        return fail(EP_ERR_UNSUPPORTED, "per-pair weights are supported for EP_BF16 only");
+    if (pair_w != nullptr && dtype == EP_FP8_PREQUANT)
+        return fail(EP_ERR_UNSUPPORTED, "per-pair weights need EP_BF16 or EP_FP8_QUANTIZE");
     if (T > 0 && (x == nullptr || !aligned(x, 16))) return fail(EP_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
     if (recv == nullptr || !aligned(recv, 16)) return fail(EP_ERR_INVALID_ARG, "recv must be non-NULL and 16-byte aligned");
     if (fp8 && (recv_scales == nullptr || !aligned(recv_scales, 4)))
@@ -145,7 +145,7 @@ ep_status prepare_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, co
     if (dtype == EP_BF16)
         *kind = pair_w ? ep::kDispatchBf16Weighted : ep::kDispatchBf16;
     else if (dtype == EP_FP8_QUANTIZE)
-        *kind = ep::kDispatchFp8Quant;
+        *kind = pair_w ? ep::kDispatchFp8QuantWeighted : ep::kDispatchFp8Quant;
     else
         *kind = ep::kDispatchFp8Copy;
     return EP_OK;
@@ -350,10 +350,8 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
 
 ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* grad_out, const float* topk_w,
                               void* grad_y, float* grad_y_scales, void* stream) {
-    if (topk_w != nullptr && dtype == EP_FP8_QUANTIZE)
-        return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward with FP8 quantisation is not supported");
     if (topk_w != nullptr && dtype == EP_FP8_PREQUANT)
-        return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward needs EP_BF16");
+        return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward needs EP_BF16 or EP_FP8_QUANTIZE");
     return do_dispatch(h, dtype, grad_out, nullptr, topk_w, grad_y, grad_y_scales, (hipStream_t)stream);
 }
 

@@ -29,13 +29,14 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
     float my_w = 0.0f;
     if (lane < a.k) {
         my_s = a.slot[(int64_t)t * a.k + lane];
-        if (KIND == kDispatchBf16Weighted) my_w = a.pair_w[(int64_t)t * a.k + lane];
+        if (KIND == kDispatchBf16Weighted || KIND == kDispatchFp8QuantWeighted)
+            my_w = a.pair_w[(int64_t)t * a.k + lane];
     }
     dispatch_token<KIND>(a, t, 0, dispatch_nvec<KIND>(a), my_s, my_w);
 }
 
 hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream) {
-    const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy;
+    const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy || kind == kDispatchFp8QuantWeighted;
     const int nvec = fp8 ? a.H / 16 : a.H / 8;
     int threads = ((nvec + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
@@ -52,9 +53,14 @@ hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream) 
         case kDispatchFp8Quant:
             hipLaunchKernelGGL(k_dispatch<kDispatchFp8Quant>, dim3(grid), dim3(threads), 0, stream, a);
             break;
-        default:
+        case kDispatchFp8Copy:
             hipLaunchKernelGGL(k_dispatch<kDispatchFp8Copy>, dim3(grid), dim3(threads), 0, stream, a);
             break;
+        case kDispatchFp8QuantWeighted:
+            hipLaunchKernelGGL(k_dispatch<kDispatchFp8QuantWeighted>, dim3(grid), dim3(threads), 0, stream, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

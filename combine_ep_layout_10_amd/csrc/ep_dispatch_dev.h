@@ -37,7 +37,9 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float f[8]) {
     return o;
 }
 
-constexpr bool dispatch_is_fp8(int kind) { return kind == kDispatchFp8Quant || kind == kDispatchFp8Copy; }
+constexpr bool dispatch_is_fp8(int kind) {
+    return kind == kDispatchFp8Quant || kind == kDispatchFp8Copy || kind == kDispatchFp8QuantWeighted;
+}
 
 // Zero-fills receive rows [r0, r1) (data and, for FP8, scales) with the
 // whole block.
@@ -66,7 +68,7 @@ struct DispatchRaw {
     float scale;
 };
 struct DispatchVec {
-    uint4 v;
+    uint4 v, v1;  // v1: second half of the 16 values (weighted FP8 only)
     float scale;
 };
 
@@ -81,7 +83,7 @@ __device__ __forceinline__ DispatchRaw dispatch_load(const DispatchArgs& a, int 
     if (!act) return r;
     if (KIND == kDispatchBf16 || KIND == kDispatchBf16Weighted) {
         r.v0 = ((const uint4*)((const char*)a.x + (int64_t)t * 2 * a.H))[c];
-    } else if (KIND == kDispatchFp8Quant) {
+    } else if (KIND == kDispatchFp8Quant || KIND == kDispatchFp8QuantWeighted) {
         const uint4* src = (const uint4*)((const char*)a.x + (int64_t)t * 2 * a.H);
         r.v0 = src[2 * c];
         r.v1 = src[2 * c + 1];
@@ -92,31 +94,40 @@ __device__ __forceinline__ DispatchRaw dispatch_load(const DispatchArgs& a, int 
     return r;
 }
 
-// Turns loaded bytes into what is stored. FP8 quantise: amax of the 1x128
-// block over eight consecutive lanes (DPP), scale = amax / 448, codes =
-// E4M3(x / scale); every lane of the wave must call it (inactive lanes hold
-// zeros), and vectors must be grouped in aligned runs of eight.
+// Quantises this lane's 16 values of a 1x128 block held by eight consecutive
+// lanes: amax over the block (DPP across the eight lanes), scale = amax /
+// 448, codes = E4M3(x / scale) with both divisions IEEE binary32; an
+// all-zero block gives scale 0 and zero codes. Every lane of the wave must
+// call it (inactive lanes hold zeros).
+__device__ __forceinline__ uint4 quantize16(const float f[16], float& scale_out) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = max8_dpp(amax);
+    const float scale = amax / 448.0f;
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+    if (amax != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w4[i >> 2] |= f32_to_e4m3_sat(f[i] / scale) << (8 * (i & 3));
+    }
+    scale_out = scale;
+    return make_uint4(w4[0], w4[1], w4[2], w4[3]);
+}
+
+// Turns loaded bytes into what is stored. FP8 quantise: the 1x128 block
+// quantiser above; vectors must be grouped in aligned runs of eight. The
+// weighted FP8 kind keeps the values: each pair is quantised at the store.
 template <int KIND>
 __device__ __forceinline__ DispatchVec dispatch_encode(const DispatchRaw& r) {
     DispatchVec d;
     d.v = r.v0;
+    d.v1 = r.v1;
     d.scale = r.scale;
     if (KIND == kDispatchFp8Quant) {
         float f[16];
         unpack_bf16x8(r.v0, f);
         unpack_bf16x8(r.v1, f + 8);
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = max8_dpp(amax);
-        const float scale = amax / 448.0f;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        if (amax != 0.0f) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w4[i >> 2] |= f32_to_e4m3_sat(f[i] / scale) << (8 * (i & 3));
-        }
-        d.v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        d.scale = scale;
+        d.v = quantize16(f, d.scale);
     }
     return d;
 }
@@ -131,6 +142,29 @@ __device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const Disp
     constexpr bool kFp8 = dispatch_is_fp8(KIND);
     const int64_t row_out = kFp8 ? (int64_t)a.H : 2 * (int64_t)a.H;
     const int nb = a.H / 128;
+    if (KIND == kDispatchFp8QuantWeighted) {
+        // Each pair's copy is bf16(w * x), quantised with its own scales. The
+        // pair loop is uniform (slots are broadcast), so every lane of the
+        // wave takes part in each block reduction; `act` guards the stores.
+        float f[16];
+        unpack_bf16x8(d.v, f);
+        unpack_bf16x8(d.v1, f + 8);
+        for (int j = 0; j < a.k; ++j) {
+            const int s = __builtin_amdgcn_readlane(my_s, j);
+            if (s < 0) continue;
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+            float g[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) g[i] = bf16_to_f32(f32_to_bf16_rne(wj * f[i]));
+            float scale;
+            const uint4 o = quantize16(g, scale);
+            if (act) {
+                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
+                if ((c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = scale;
+            }
+        }
+        return;
+    }
     float f[8];
     if (KIND == kDispatchBf16Weighted) unpack_bf16x8(d.v, f);
     if (!act) return;

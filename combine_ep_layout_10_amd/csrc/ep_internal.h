@@ -45,7 +45,15 @@ struct LayoutArgs {
     uint32_t* fpart;  // [nblk] per-block error bits
 };
 
-enum DispatchKind { kDispatchBf16 = 0, kDispatchBf16Weighted = 1, kDispatchFp8Quant = 2, kDispatchFp8Copy = 3 };
+// kDispatchFp8QuantWeighted: combine_backward of a weighted combine with FP8
+// output, each pair's copy bf16(w * x) quantised with its own 1x128 scales.
+enum DispatchKind {
+    kDispatchBf16 = 0,
+    kDispatchBf16Weighted = 1,
+    kDispatchFp8Quant = 2,
+    kDispatchFp8Copy = 3,
+    kDispatchFp8QuantWeighted = 4
+};
 
 struct DispatchArgs {
     const void* x;

@@ -219,10 +219,12 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
                                void* grad_x, float* grad_topk_w, void* stream);
 
 /* README combine_backward: the backward of a combine is a dispatch of the
- * output gradient on the same handle. With topk_w (EP_BF16 only), the copy
- * for pair (t, j) is bf16(topk_w[t, j] * float(grad_out[t, c])), the
- * gradient of the weighted combine; EP_FP8_QUANTIZE with topk_w returns
- * EP_ERR_UNSUPPORTED. */
+ * output gradient on the same handle. With topk_w, the copy for pair (t, j)
+ * is the gradient of the weighted combine, bf16(topk_w[t, j] *
+ * float(grad_out[t, c])) (one binary32 multiply, round to nearest even);
+ * with EP_FP8_QUANTIZE that BF16 copy is then quantised per 1x128 block as
+ * ep_dispatch quantises x, each pair with its own scales. EP_FP8_PREQUANT
+ * with topk_w returns EP_ERR_UNSUPPORTED. */
 ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* grad_out,
                               const float* topk_w, void* grad_y, float* grad_y_scales,
                               void* stream);

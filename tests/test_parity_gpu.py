@@ -293,8 +293,13 @@ def test_backward_duals():
     gq, gs = ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE)
     assert np.array_equal(host(gq)[rows], q[rows])
     assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
+    # weighted FP8: each pair's bf16(w * g) quantised with its own scales
+    q, s = oracle.combine_backward_fp8(lay, go, k, w)
+    gq, gs = ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE, to_dev(w))
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
     with pytest.raises(Exception):
-        ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE, to_dev(w))
+        ops.combine_backward(h, to_dev(np.zeros((T, H), np.uint8)), ops.FP8_PREQUANT, to_dev(w))
 
 
 def _weight_grad_bound(H, g, y, slot):
@@ -356,6 +361,22 @@ def test_combine_weight_grad_v3_full_size():
     g = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
     err, bound = _check_weight_grad(h, lay, g, inp["y"], wl.k)
     log("v3 weight grad: max err/bound %.3g" % float((err / bound).max()))
+
+
+def test_combine_backward_fp8_weighted_v3_shape():
+    """Weighted FP8 combine_backward on 1024 tokens of the 7168 x top-8,
+    256-expert shape (8 pairs per token, each with its own scales)."""
+    wl = WORKLOADS["v3"].with_tokens(1024)
+    inp = make_inputs(wl, with_y=False)
+    lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, inp["topk_idx"], inp["topk_w"])
+    h = ops.layout(cfg_of(wl), to_dev(inp["topk_idx"]), to_dev(inp["topk_w"]))
+    rng = np.random.default_rng(43)
+    go = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
+    q, s = oracle.combine_backward_fp8(lay, go, wl.k, inp["topk_w"])
+    gq, gs = ops.combine_backward(h, to_dev_bf16(go), ops.FP8_QUANTIZE, to_dev(inp["topk_w"]))
+    rows = np.arange(lay["rows"])
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
 
 
 def test_fp8_prequant_passthrough():
