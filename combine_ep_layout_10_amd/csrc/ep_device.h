@@ -21,26 +21,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// binary32 -> OCP E4M3FN byte, round to nearest even, saturating at +-448.
-// |v| >= 2^-6 (normal E4M3): the E4M3 code of a normal value is the binary32
-// pattern's exponent rebiased (127 -> 7) followed by its top three mantissa
-// bits, so rounding the pattern at bit 20 (RNE on the integer) and
-// subtracting the bias difference (120 << 3) gives the code, with mantissa
-// carries stepping the exponent. |v| < 2^-6: the E4M3 subnormals are
-// m * 2^-9, so the code is |v| * 512 rounded to the nearest even integer
-// (0..8; 8 is the smallest normal 0x08). Codes above 0x7E (448) saturate.
-__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    float af = __uint_as_float(a);
-    uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t sub = (uint32_t)__builtin_rintf(af * 512.0f);
-    uint32_t code = af < 0.015625f ? sub : normal;
-    code = code > 0x7Eu ? 0x7Eu : code;
-    return sign | code;
-}
-
 // ---------------------------------------------------------------- memory
 
 // Streaming (non-temporal) 16-byte accesses for data touched once: on gfx950

@@ -441,6 +441,45 @@ def test_fp8_codec_all_bf16_patterns():
         assert np.array_equal(host(gs)[:T].view(np.uint32), s[:T].view(np.uint32)), factor
 
 
+def test_fp8_quantiser_every_pair():
+    """Every pair of finite bf16 magnitudes |x| <= amax through the GPU FP8
+    dispatch, bit-exact against the oracle: for each non-negative finite
+    bf16 value a (the block's amax, element 0), blocks of 127 further
+    elements hold every bf16 magnitude <= a, signs alternating so each value
+    meets both signs. 4.2M blocks of 128 in five launches."""
+    vals = np.arange(0x7F80, dtype=np.uint16)          # +0 .. largest finite, increasing
+    n = vals.size
+    nb = (np.arange(n) + 127) // 127                    # blocks needed for amax index i: ceil((i+1)/127)
+    nb[0] = 0                                           # amax 0: all-zero blocks are tested elsewhere
+    bounds = np.searchsorted(np.cumsum(nb), np.linspace(0, nb.sum(), 6)[1:-1])
+    edges = [1] + [int(b) for b in bounds] + [n]
+    for c in range(len(edges) - 1):
+        i0, i1 = edges[c], edges[c + 1]
+        cnt = nb[i0:i1]
+        amax_idx = np.repeat(np.arange(i0, i1, dtype=np.int32), cnt)
+        first = np.repeat(np.cumsum(cnt) - cnt, cnt)
+        off = (np.arange(amax_idx.size) - first).astype(np.int32)
+        idx = off[:, None] * 127 + np.arange(127, dtype=np.int32)[None, :]
+        valid = idx <= amax_idx[:, None]
+        xs = np.where(valid, vals[np.minimum(idx, n - 1)], 0).astype(np.uint16)
+        xs |= (((idx + amax_idx[:, None]) & 1).astype(np.uint16) << 15) & np.where(valid, 0x8000, 0).astype(np.uint16)
+        del idx, valid
+        x = np.concatenate([vals[amax_idx][:, None], xs], axis=1)
+        del xs
+        T = x.shape[0]
+        log("fp8 every pair: chunk %d, amax index %d..%d, %d blocks" % (c, i0, i1, T))
+        topk = np.zeros((T, 1), np.int64)
+        lay = oracle.layout(0, T, 1, 1, 1, 1, 0, topk)
+        q, sc = oracle.dispatch_fp8(lay, x, 1)
+        cfg = ops.Config(max_tokens=T, hidden=128, num_experts=1, num_topk=1)
+        h = ops.layout(cfg, to_dev(topk))
+        gq, gs = ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE)
+        assert np.array_equal(host(gq), q), c
+        assert np.array_equal(host(gs).view(np.uint32), sc.view(np.uint32)), c
+        del q, sc, gq, gs, x
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- determinism
 
 def test_repeat_is_bit_identical():
