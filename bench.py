@@ -47,6 +47,8 @@ def parse():
                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
     p.add_argument("--graph", action="store_true",
                    help="capture one step in a HIP graph and time K replays (launch-bound shapes)")
+    p.add_argument("--bound", action="store_true",
+                   help="time steps issued through bound calls (arguments converted once)")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip timing a plain 1 GiB device-to-device copy for reference")
     return p.parse_args()
@@ -182,9 +184,17 @@ def main():
             step()
         torch.cuda.synchronize()
 
+    bound = None
+    if args.bound:
+        fwd_call, hb = ops.bind_dispatch_forward(cfg, idx, x, dtype, recv, rs, topk_w=w, workspace=ws)
+        bound = (fwd_call, ops.bind_combine(hb, y, out, topk_w=w))
+
     def run_step():
         if graph is not None:
             graph.replay()
+        elif bound is not None:
+            bound[0]()
+            bound[1]()
         else:
             step()
 
@@ -194,7 +204,7 @@ def main():
     torch.cuda.synchronize()
     # Timed region: exactly K steps. Eager steps carry one event pair around
     # the dominant kernel (recorded on the kernels' stream); graph replays
-    # carry none.
+    # and bound calls carry none.
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -203,6 +213,10 @@ def main():
     for i in range(args.steps):
         if graph is not None:
             graph.replay()
+            continue
+        if bound is not None:
+            bound[0]()
+            bound[1]()
             continue
         e0, e1 = dom_ev[i]
         if dominant == "combine":
@@ -219,7 +233,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_live_ms = None if graph is not None else float(np.mean([a.elapsed_time(b) for a, b in dom_ev]))
+    live = graph is None and bound is None
+    dom_live_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_ev])) if live else None
     # Per-kernel durations: K more steps as separate layout / dispatch /
     # combine calls with events between them (not part of the timed region).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -297,7 +312,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "graph": bool(args.graph), "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
+        "config": {"workload": wl.name, "launch": "graph" if args.graph else ("bound" if args.bound else "eager"), "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
                    "expert_alignment": wl.A, "dests": wl.D, "mode": "fixed" if wl.mode else "compact",
                    "dispatch": "fp8_e4m3_1x128" if fp8 else "bf16", "combine": "bf16", "routing": wl.routing},
         "roofline": roofline,
@@ -306,6 +321,7 @@ def main():
             "layout_us": round(lay_ms * 1e3, 2), "dispatch_us": round(dis_ms * 1e3, 2),
             "combine_us": round(com_ms * 1e3, 2), "gpu_step_us": round(gpu_ms * 1e3, 2),
             "dispatch_forward_plus_combine_us": round(step_ev_ms * 1e3, 2), "graph": bool(args.graph),
+            "bound": bool(args.bound),
             "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
             "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
             "bytes": nbytes, "kernel_hash": khash,

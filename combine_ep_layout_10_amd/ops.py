@@ -311,3 +311,76 @@ def combine_weight_grad(h: Handle, grad_out: torch.Tensor, y: torch.Tensor,
     F.ep_combine_weight_grad(h.c, _dev(grad_out, "grad_out", torch.bfloat16), _dev(y, "y", torch.bfloat16),
                              _dev(grad_topk_w, "grad_topk_w", torch.float32), _stream())
     return grad_topk_w
+
+
+# ---------------------------------------------------------------- bound calls
+
+class BoundCall:
+    """One entry point with every argument converted once. Each call
+    re-issues the same C function on the same buffers and stream (their
+    contents are read when the kernels run), so it costs one foreign call:
+    the low-latency form of the README's cached-handle decode loop, for
+    callers that reuse their buffers from step to step. The tensors stay
+    referenced for the object's lifetime."""
+
+    def __init__(self, fn, args, name: str, keep):
+        self._fn = fn
+        self._args = args
+        self._name = name
+        self._keep = keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != F.EP_OK:
+            raise F.EPError(st, self._name, F.last_error_message())
+
+
+def bind_dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype: int, recv: torch.Tensor,
+                          recv_scales: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                          x_scales: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Bound ep_dispatch_forward on fixed buffers. Returns (call, handle):
+    every call() rebuilds the layout from topk_idx's current contents and
+    dispatches x into recv; `handle` (shared by all calls) describes it."""
+    import ctypes
+    T, H, R = int(topk_idx.shape[0]), cfg.hidden, cfg.recv_rows_bound()
+    idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
+    if topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+        raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
+    _need(topk_w, tuple(topk_idx.shape), "topk_w")
+    _need(x, (T, H), "x")
+    _need(recv, (R, H), "recv")
+    fp8 = dtype != BF16
+    if fp8:
+        _need(recv_scales, (R, H // 128), "recv_scales")
+    if dtype == FP8_PREQUANT:
+        _need(x_scales, (T, H // 128), "x_scales")
+    if workspace is None:
+        workspace = new_workspace(cfg, topk_idx.device)
+    c = _c_config(cfg)
+    hc = F.ep_handle()
+    xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
+    vp = ctypes.c_void_p
+    args = (ctypes.byref(c), ctypes.c_int32(T), vp(_dev(topk_idx, "topk_idx", idx_dtype)),
+            vp(_opt(topk_w, "topk_w", torch.float32)), vp(_dev(workspace, "workspace", torch.uint8)),
+            ctypes.c_size_t(workspace.numel()), ctypes.c_int(dtype), vp(_dev(x, "x", xdt)),
+            vp(_opt(x_scales, "x_scales", torch.float32)),
+            vp(_dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16)),
+            vp(_opt(recv_scales, "recv_scales", torch.float32)), ctypes.byref(hc), vp(_stream()))
+    call = BoundCall(F.lib().ep_dispatch_forward, args, "ep_dispatch_forward",
+                     (cfg, c, hc, topk_idx, topk_w, x, x_scales, recv, recv_scales, workspace))
+    call()
+    return call, Handle(cfg, hc, workspace)
+
+
+def bind_combine(h: Handle, y: torch.Tensor, out: torch.Tensor, topk_w: Optional[torch.Tensor] = None):
+    """Bound ep_combine on fixed buffers and on h's handle structure (which a
+    bound dispatch_forward rewrites in place), issued with call()."""
+    import ctypes
+    T, H = h.num_tokens, h.cfg.hidden
+    _need(y, (h.cfg.recv_rows_bound(), H), "y")
+    _need(topk_w, (T, h.cfg.num_topk), "topk_w")
+    _need(out, (T, H), "out")
+    vp = ctypes.c_void_p
+    args = (ctypes.byref(h.c), vp(_dev(y, "y", torch.bfloat16)), vp(_opt(topk_w, "topk_w", torch.float32)),
+            vp(_dev(out, "out", torch.bfloat16)), None, None, vp(_stream()))
+    return BoundCall(F.lib().ep_combine, args, "ep_combine", (h, y, out, topk_w))

@@ -261,6 +261,44 @@ def test_dispatch_forward_graph_replay():
         assert np.array_equal(got[3], ref[3]), rep
 
 
+def test_bound_calls_match_eager():
+    """Bound dispatch_forward + combine (arguments converted once) on fixed
+    buffers: three steps with new routing, weights and x copied in between,
+    each equal to the eager calls and the oracle's slots."""
+    wl = WORKLOADS["decode"]
+    cfg = cfg_of(wl)
+    R = cfg.recv_rows_bound()
+    rng = np.random.default_rng(23)
+    idx_s = torch.zeros((wl.T, wl.k), dtype=torch.int64, device="cuda")
+    w_s = torch.zeros((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    x_s = torch.zeros((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    y = to_dev_bf16(f32_to_bf16_bits(rng.standard_normal((R, wl.H)).astype(np.float32)))
+    recv = torch.empty((R, wl.H), dtype=torch.uint8, device="cuda")
+    rs = torch.empty((R, wl.H // 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    fwd, h = ops.bind_dispatch_forward(cfg, idx_s, x_s, ops.FP8_QUANTIZE, recv, rs, topk_w=w_s)
+    comb = ops.bind_combine(h, y, out, topk_w=w_s)
+    for rep in range(3):
+        idx = np.stack([rng.permutation(wl.E)[:wl.k] for _ in range(wl.T)]).astype(np.int64)
+        w = rng.random((wl.T, wl.k)).astype(np.float32)
+        x = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
+        idx_s.copy_(to_dev(idx))
+        w_s.copy_(to_dev(w))
+        x_s.copy_(to_dev_bf16(x))
+        fwd()
+        comb()
+        torch.cuda.synchronize()
+        got = (host(h.slot).copy(), host(recv).copy(), host(rs).copy(), bf16_host(out).copy())
+        he, re_, se = ops.dispatch_forward(cfg, idx_s, x_s, ops.FP8_QUANTIZE, topk_w=w_s)
+        oe = ops.combine(he, y, w_s)
+        lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, idx, w)
+        rows = written_rows(lay)
+        assert np.array_equal(got[0], lay["slot"]), rep
+        assert np.array_equal(got[1][rows], host(re_)[rows]), rep
+        assert np.array_equal(got[2][rows].view(np.uint32), host(se)[rows].view(np.uint32)), rep
+        assert np.array_equal(got[3], bf16_host(oe)), rep
+
+
 # ---------------------------------------------------------------- duals
 
 def test_backward_duals():
