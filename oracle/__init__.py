@@ -65,6 +65,10 @@ def _load():
     lib.ora_combine.argtypes = [i32, i32, i32, P, P, P, P, P, P]
     lib.ora_combine_backward_fp8.restype = None
     lib.ora_combine_backward_fp8.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, i32, P, P]
+    lib.ora_grouped_gemm_fp8.restype = None
+    lib.ora_grouped_gemm_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
+    lib.ora_grouped_gemm_fp8_at.restype = None
+    lib.ora_grouped_gemm_fp8_at.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.ora_combine_weight_grad.restype = None
     lib.ora_combine_weight_grad.argtypes = [i32, i32, i32, P, P, P, P]
     lib.ora_e4m3_encode_many.restype = None
@@ -255,6 +259,33 @@ def combine_backward_fp8(lay: dict, grad_out: np.ndarray, k: int, topk_w: np.nda
     lib.ora_combine_backward_fp8(T, H, k, E, _p(g), _p(w), _p(lay["slot"]), _p(lay["cnt"]), _p(lay["pad"]),
                                  _p(lay["expert_off"]), int(bool(zero_pad)), _p(recv), _p(scales))
     return recv, scales
+
+
+def grouped_gemm_fp8(row_begin: np.ndarray, row_end: np.ndarray, a: np.ndarray, sa: np.ndarray,
+                     b: np.ndarray, sb: np.ndarray, pairs: Optional[np.ndarray] = None) -> np.ndarray:
+    """FP8 grouped GEMM over expert row ranges (see ora_grouped_gemm_fp8).
+    a [rows, K] u8, sa [rows, K/128] f32, b [E, N, K] u8, sb [E, N/128, K/128]
+    f32. Returns C [rows, N] bf16 bits (rows outside every range 0xFFFF), or,
+    with pairs [n, 2] int64 (r, n), the bf16 bits of those outputs."""
+    lib = _load()
+    a = _c(a, np.uint8)
+    sa = _c(sa, np.float32)
+    b = _c(b, np.uint8)
+    sb = _c(sb, np.float32)
+    rb = _c(row_begin, np.int32)
+    re_ = _c(row_end, np.int32)
+    E, N, K = b.shape
+    if K % 128 or N % 128 or a.shape[1] != K or sa.shape != (a.shape[0], K // 128) or sb.shape != (E, N // 128, K // 128):
+        raise ValueError("grouped GEMM shapes disagree")
+    if pairs is None:
+        C = np.full((a.shape[0], N), 0xFFFF, np.uint16)
+        lib.ora_grouped_gemm_fp8(E, K, N, _p(rb), _p(re_), _p(a), _p(sa), _p(b), _p(sb), _p(C))
+        return C
+    pr = _c(pairs, np.int64)
+    out = np.empty(pr.shape[0], np.uint16)
+    lib.ora_grouped_gemm_fp8_at(E, K, N, _p(rb), _p(re_), _p(a), _p(sa), _p(b), _p(sb), _p(pr), pr.shape[0],
+                                _p(out))
+    return out
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:

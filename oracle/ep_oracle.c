@@ -473,6 +473,84 @@ void ora_combine_weight_grad(int T, int H, int k, const uint16_t* grad_out, cons
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* Consumer: FP8 grouped GEMM over the aligned expert-major layout          */
+/* ---------------------------------------------------------------------- */
+
+/* binary64 -> bfloat16, round to nearest even, directly from the double (no
+ * intermediate binary32 rounding). Finite inputs within the bf16 range. */
+static uint16_t ora_bf16_rne_f64(double v) {
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0x0000;
+    uint16_t sign = v < 0 ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                      /* a = f * 2^e, f in [0.5, 1) */
+    int q = e - 8;                     /* bf16 keeps 8 significant bits */
+    if (q < -133)
+        q = -133;                      /* subnormal bf16 spacing 2^-133 */
+    double m = ldexp(a, -q);           /* exact */
+    double r = floor(m);
+    double frac = m - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0))
+        r += 1.0;
+    double val = ldexp(r, q);
+    float f = (float)val;              /* exact: val has <= 9 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* The grouped GEMM the layout exists for (README: per-expert received-token
+ * counts "for GEMM", rows padded to expert_alignment; "New features": the
+ * new GEMM layout): rows of expert e, [row_begin[e], row_end[e]), times that
+ * expert's weight matrix. A is the dispatched E4M3 codes [rows, K] with
+ * 1x128 scales sa [rows, K/128]; expert e's weights are E4M3 codes
+ * B[e] [N, K] (one row per output channel) with 128x128 block scales
+ * sb[e] [N/128, K/128]. For row r of expert e and channel n:
+ *   C[r, n] = bf16( sum_kb sa[r, kb] * sb[e, n/128, kb]
+ *                          * sum_{k in block kb} A[r, k] * B[e, n, k] )
+ * with decoded code values, in binary64 (each block sum of 128 products of
+ * E4M3 values is exact in binary64), rounded once to bf16. */
+static double ora_gemm_one(int K, int N, int e, int64_t r, int64_t n, const uint8_t* A, const float* sa,
+                           const uint8_t* B, const float* sb) {
+    int kb_n = K / 128, nb_n = N / 128;
+    const uint8_t* a = A + r * (int64_t)K;
+    const uint8_t* b = B + ((int64_t)e * N + n) * (int64_t)K;
+    double acc = 0.0;
+    for (int kb = 0; kb < kb_n; ++kb) {
+        double blk = 0.0;
+        for (int k = kb * 128; k < kb * 128 + 128; ++k)
+            blk += ora_e4m3_code_value(a[k] & 0x7F) * ((a[k] & 0x80) ? -1.0 : 1.0)
+                   * ora_e4m3_code_value(b[k] & 0x7F) * ((b[k] & 0x80) ? -1.0 : 1.0);
+        acc += (double)sa[r * kb_n + kb] * (double)sb[((int64_t)e * nb_n + n / 128) * kb_n + kb] * blk;
+    }
+    return acc;
+}
+
+/* Every row of every expert range: C [rows, N] bf16. */
+void ora_grouped_gemm_fp8(int E, int K, int N, const int32_t* row_begin, const int32_t* row_end,
+                          const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, uint16_t* C) {
+    for (int e = 0; e < E; ++e)
+        for (int64_t r = row_begin[e]; r < row_end[e]; ++r)
+            for (int64_t n = 0; n < N; ++n)
+                C[r * N + n] = ora_bf16_rne_f64(ora_gemm_one(K, N, e, r, n, A, sa, B, sb));
+}
+
+/* Selected outputs only: pairs[2i] = r, pairs[2i+1] = n; out[i] = C[r, n]
+ * (0 when r lies in no expert range). For checking full-size results. */
+void ora_grouped_gemm_fp8_at(int E, int K, int N, const int32_t* row_begin, const int32_t* row_end,
+                             const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                             const int64_t* pairs, int64_t n_pairs, uint16_t* out) {
+    for (int64_t i = 0; i < n_pairs; ++i) {
+        int64_t r = pairs[2 * i], n = pairs[2 * i + 1];
+        int e = 0;
+        while (e < E && !(r >= row_begin[e] && r < row_end[e]))
+            ++e;
+        out[i] = e < E ? ora_bf16_rne_f64(ora_gemm_one(K, N, e, r, n, A, sa, B, sb)) : 0;
+    }
+}
+
 /* Batch form of the codec for tests: encode n binary32 values. */
 void ora_e4m3_encode_many(const float* v, int64_t n, uint8_t* q) {
     for (int64_t i = 0; i < n; ++i)
