@@ -84,6 +84,7 @@ _SIGNATURES = {
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),
     "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int, _P, _P, _P, _P, _P]),
     "ep_combine_weight_grad": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
+    "ep_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_handle_check": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P]),
     "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -170,6 +171,12 @@ def ep_combine_backward(h: ep_handle, dtype: int, grad_out: int, topk_w, grad_y:
 def ep_combine_weight_grad(h: ep_handle, grad_out: int, y: int, grad_topk_w: int, stream: int) -> None:
     _check(lib().ep_combine_weight_grad(ctypes.byref(h), grad_out, y, grad_topk_w, stream),
            "ep_combine_weight_grad")
+
+
+def ep_grouped_gemm_fp8(h: ep_handle, a: int, a_scales: int, b: int, b_scales: int, n: int, out: int,
+                        stream: int) -> None:
+    _check(lib().ep_grouped_gemm_fp8(ctypes.byref(h), a, a_scales, b, b_scales, int(n), out, stream),
+           "ep_grouped_gemm_fp8")
 
 
 def ep_handle_read_counts(h: ep_handle, cnt, pad, rows, stream: int) -> None:

@@ -379,6 +379,40 @@ ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const
     return EP_OK;
 }
 
+ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_scales, const void* b,
+                              const float* b_scales, int32_t n, void* out, void* stream) {
+    ep_status s = check_handle(h);
+    if (s != EP_OK) return s;
+    const ep_config& c = h->cfg;
+    if (c.hidden % 128 != 0) return fail(EP_ERR_UNSUPPORTED, "grouped GEMM needs hidden %% 128 == 0 (hidden %d)", c.hidden);
+    if (n < 128 || n % 128 != 0) return fail(EP_ERR_INVALID_ARG, "n %d must be a positive multiple of 128", n);
+    if (c.mode == EP_MODE_COMPACT && c.expert_alignment % 128 != 0)
+        return fail(EP_ERR_UNSUPPORTED, "grouped GEMM needs expert_alignment %% 128 == 0 (got %d)", c.expert_alignment);
+    if (c.mode == EP_MODE_FIXED && c.capacity % 128 != 0)
+        return fail(EP_ERR_UNSUPPORTED, "grouped GEMM needs capacity %% 128 == 0 (got %d)", c.capacity);
+    if (a == nullptr || !aligned(a, 16) || a_scales == nullptr || !aligned(a_scales, 4))
+        return fail(EP_ERR_INVALID_ARG, "a must be 16-byte aligned and a_scales non-NULL");
+    if (b == nullptr || !aligned(b, 16) || b_scales == nullptr || !aligned(b_scales, 4))
+        return fail(EP_ERR_INVALID_ARG, "b must be 16-byte aligned and b_scales non-NULL");
+    if (out == nullptr || !aligned(out, 4)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 4-byte aligned");
+    ep::GemmArgs g;
+    g.a = (const uint8_t*)a;
+    g.sa = a_scales;
+    g.b = (const uint8_t*)b;
+    g.sb = b_scales;
+    g.c = (uint16_t*)out;
+    g.expert_off = h->expert_off;
+    g.pad = h->pad;
+    g.E = c.num_experts;
+    g.K = c.hidden;
+    g.N = n;
+    g.mode = c.mode;
+    g.C = c.capacity;
+    hipError_t e = ep::launch_grouped_gemm_fp8(g, rows_bound(c), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped GEMM launch");
+    return EP_OK;
+}
+
 ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, int64_t* rows, void* stream) {
     ep_status s = check_handle(h);
     if (s != EP_OK) return s;

@@ -104,6 +104,17 @@ struct WeightGradArgs {
     int T, H, k;
 };
 
+struct GemmArgs {
+    const uint8_t* a;
+    const float* sa;
+    const uint8_t* b;
+    const float* sb;
+    uint16_t* c;
+    const int32_t* expert_off;
+    const int32_t* pad;
+    int E, K, N, mode, C;
+};
+
 // Rows of padding one dispatch block clears.
 constexpr int kPadRowsPerBlock = 16;
 
@@ -111,6 +122,7 @@ hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
 hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_weight_grad(const WeightGradArgs& a, hipStream_t stream);
+hipError_t launch_grouped_gemm_fp8(const GemmArgs& a, int64_t rows_bound, hipStream_t stream);
 // Single-launch layout + dispatch (unweighted kinds) for small batches.
 bool fused_layout_dispatch_fits(int64_t pairs, int E);
 hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, hipStream_t stream);

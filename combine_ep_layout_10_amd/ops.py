@@ -10,6 +10,7 @@ Mapping to the DeepEP README ("Interfaces and examples"):
   dispatch_backward            -> dispatch_backward (a combine)
   combine_backward             -> combine_backward (a dispatch on the handle)
   combine_weight_grad          -> the weight gradient of the weighted combine
+  grouped_gemm_fp8             -> the expert GEMM the layout is built for
   dispatch with an old Handle  -> decode_dispatch with cached_handle
 """
 from __future__ import annotations
@@ -312,6 +313,27 @@ def combine_weight_grad(h: Handle, grad_out: torch.Tensor, y: torch.Tensor,
                              _dev(grad_topk_w, "grad_topk_w", torch.float32), _stream())
     return grad_topk_w
 
+
+
+def grouped_gemm_fp8(h: Handle, a: torch.Tensor, a_scales: torch.Tensor, b: torch.Tensor, b_scales: torch.Tensor,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP8 grouped GEMM over the receive layout: out [rows bound, n] bf16,
+    rows of expert e times b[e] [n, hidden] (E4M3FN) with 1x128 row scales
+    and 128x128 weight scales."""
+    R, H, E = h.cfg.recv_rows_bound(), h.cfg.hidden, h.cfg.num_experts
+    if b.dim() != 3 or b.shape[0] != E or b.shape[2] != H:
+        raise ValueError("b must be [E, n, hidden]")
+    n = int(b.shape[1])
+    _need(a, (R, H), "a")
+    _need(a_scales, (R, H // 128), "a_scales")
+    _need(b_scales, (E, n // 128, H // 128), "b_scales")
+    if out is None:
+        out = torch.empty((R, n), dtype=torch.bfloat16, device=a.device)
+    _need(out, (R, n), "out")
+    F.ep_grouped_gemm_fp8(h.c, _dev(a, "a", torch.uint8), _dev(a_scales, "a_scales", torch.float32),
+                          _dev(b, "b", torch.uint8), _dev(b_scales, "b_scales", torch.float32), n,
+                          _dev(out, "out", torch.bfloat16), _stream())
+    return out
 
 # ---------------------------------------------------------------- bound calls
 

@@ -247,6 +247,31 @@ ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* gr
 ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const void* y,
                                  float* grad_topk_w, void* stream);
 
+/* FP8 grouped GEMM over the receive layout: the consumer the layout is built
+ * for (README: per-expert received-token counts "for GEMM", rows padded to
+ * expert_alignment; "New features": EPv2's new GEMM layout). For every row r
+ * of expert e and output channel c < n:
+ *   out[r, c] = bf16( sum_kb a_scales[r, kb] * b_scales[e, c/128, kb]
+ *                            * sum_{k in block kb} a[r, k] * b[e, c, k] )
+ * accumulated in binary32 (MFMA partial sums per 128-wide K block, each
+ * promoted with one binary32 product of the two scales and one FMA), rounded
+ * to nearest even.
+ *   a          device E4M3FN [rows bound, hidden]: the FP8 dispatch's recv.
+ *   a_scales   device binary32 [rows bound, hidden/128]: its recv_scales.
+ *   b          device E4M3FN [E, n, hidden]: expert e's weights, one row of
+ *              hidden codes per output channel.
+ *   b_scales   device binary32 [E, n/128, hidden/128]: 128x128 block scales.
+ *   out        device bf16 [rows bound, n]. COMPACT: every row below
+ *              expert_off[E] is written (padding rows too: zero codes give
+ *              zero). FIXED: expert e's rows [e*C, e*C + ceil(pad[e]/128)*128)
+ *              are written; those at or past e*C + pad[e] depend on whatever
+ *              the receive rows hold. Other rows are not touched.
+ * Requires hidden % 128 == 0, n % 128 == 0, and expert_alignment % 128 == 0
+ * (COMPACT) or capacity % 128 == 0 (FIXED), so that every 128-row tile
+ * belongs to one expert; otherwise EP_ERR_UNSUPPORTED. */
+ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_scales, const void* b,
+                              const float* b_scales, int32_t n, void* out, void* stream);
+
 /* Copies cnt and pad (host arrays of E, either may be NULL) and the row
  * total R (host, may be NULL) to the host. Synchronises the stream: this is
  * the README's "CPU sync" of a non-cached dispatch. */
