@@ -15,7 +15,8 @@ stream the kernels run on (--graph replays a captured step instead; the
 per-kernel times then come from an evented eager pass).
 `cpu_baseline` times the single-threaded CPU oracle on the same inputs.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--graph | --bound]
+    python bench.py --step gemm [--gemm-n 4096]   # the FP8 grouped GEMM on the receive layout
 """
 from __future__ import annotations
 
@@ -31,8 +32,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch/combine effective GB/s + % of HBM peak, 8K tok×7168 top-8"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip", "ep_device.h",
-                  "ep_layout_dev.h", "ep_dispatch_dev.h"]
+KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip", "ep_gemm.hip",
+                  "ep_device.h", "ep_layout_dev.h", "ep_dispatch_dev.h"]
 
 
 def parse():
@@ -41,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="v3")
+    p.add_argument("--step", default="path", choices=["path", "gemm"],
+                   help="path: layout + dispatch + combine (the headline); gemm: the FP8 grouped GEMM consumer")
+    p.add_argument("--gemm-n", type=int, default=4096, help="output channels per expert for --step gemm")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--calib-copy", action="store_true",
@@ -103,6 +107,9 @@ def main():
     import torch
     from ep_workloads import WORKLOADS, make_inputs, draw_routing, draw_weights, draw_hidden, _streams
     from combine_ep_layout_10_amd import ops
+
+    if args.step == "gemm":
+        return bench_gemm(args)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -327,6 +334,106 @@ def main():
             "bytes": nbytes, "kernel_hash": khash,
             "copy_1GiB_GBps": copy_ceiling,
         },
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_gemm(args):
+    """The FP8 grouped GEMM over the receive layout of a workload: its FP8
+    dispatch output [rows, H] (1x128 scales) times a seeded random E4M3 weight
+    matrix [N, H] per expert (128x128 scales). One step = one GEMM launch.
+    Algorithmic flops = 2 * pairs * N * H (the routed rows; padding rows of
+    the aligned layout are computed too and reported separately)."""
+    import numpy as np
+    import torch
+    from ep_workloads import WORKLOADS, draw_routing, draw_weights, draw_hidden, _streams
+    from combine_ep_layout_10_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    if wl.dispatch != "fp8":
+        print("--step gemm needs an FP8 workload (v3, skewed_v3, decode)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    N, H = args.gemm_n, wl.H
+    sx, sr, sl, so, sy = _streams(0)
+    x_h = draw_hidden(wl, sx, so)
+    idx_h = draw_routing(wl, sr)
+    cfg = ops.Config(max_tokens=wl.T, hidden=wl.H, num_experts=wl.E, num_topk=wl.k, num_dests=wl.D,
+                     expert_alignment=wl.A, capacity=wl.C, mode=wl.mode, idx_bits=64)
+    x = torch.from_numpy(x_h.view(np.int16)).view(torch.bfloat16).to(dev)
+    h, q, s = ops.dispatch_forward(cfg, torch.from_numpy(idx_h).to(dev), x, ops.FP8_QUANTIZE)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    c = torch.randint(0, 254, (wl.E, N, H), dtype=torch.uint8, device=dev, generator=gen)
+    b = torch.where(c >= 0x7F, c + 1, c)          # every E4M3FN code but the NaN patterns
+    del c
+    sb = torch.rand((wl.E, N // 128, H // 128), device=dev, generator=gen) * 1e-2 + 1e-3
+    out = torch.empty((cfg.recv_rows_bound(), N), dtype=torch.bfloat16, device=dev)
+    cnt, pad, R = h.read_counts()
+    pairs = int(cnt.sum()) if wl.mode == 0 else int(pad.sum())
+    rows = R if wl.mode == 0 else int(sum(-(-p // 128) * 128 for p in pad))
+    flops = 2.0 * pairs * N * H
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ops.grouped_gemm_fp8(h, q, s, b, sb, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        ops.grouped_gemm_fp8(h, q, s, b, sb, out=out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in ev]))
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        qh, sh = q.cpu().numpy(), s.cpu().numpy()
+        off = h.expert_off.cpu().numpy()
+        rng = np.random.default_rng(0)
+        samples = []                              # inputs copied to the host before the timed loop
+        for _ in range(64):
+            r = int(rng.integers(0, int(off[-1])))
+            n0 = int(rng.integers(0, N // 128)) * 128
+            e = int(np.searchsorted(off, r, side="right") - 1)
+            a1 = np.zeros((128, H), np.uint8)
+            a1[0] = qh[r]
+            s1 = np.zeros((128, H // 128), np.float32)
+            s1[0] = sh[r]
+            samples.append((a1, s1, b[e:e + 1, n0:n0 + 128].cpu().numpy(),
+                            sb[e:e + 1, n0 // 128:n0 // 128 + 1].cpu().numpy()))
+        rb, re_ = np.array([0], np.int32), np.array([1], np.int32)
+        m = 0
+        c0 = time.perf_counter()
+        while time.perf_counter() - c0 < args.cpu_budget_s / 2:
+            a1, s1, b1, sb1 = samples[(m // 128) % len(samples)]
+            oracle.grouped_gemm_fp8(rb, re_, a1, s1, b1, sb1)
+            m += 128
+        cpu_s = time.perf_counter() - c0
+        cpu = {"value": round(2.0 * m * H / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": "%d outputs (128-channel pieces of 64 random rows) of the same GEMM in %.1f s, "
+                         "single-threaded C oracle in binary64" % (m, cpu_s)}
+    res = {
+        "metric": "FP8 grouped GEMM TFLOP/s on the receive layout", "value": round(tflops, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 x fp8_e4m3 -> f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_gemm", "tokens": wl.T, "hidden": H, "experts": wl.E, "topk": wl.k,
+                   "n": N, "pairs": pairs, "rows_computed": rows, "expert_alignment": wl.A},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 5000.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 5000.0, 4), "traffic": None, "kernel": "k_grouped_gemm_fp8",
+                     "algorithmic_flops_per_launch": flops, "avg_launch_us": round(launch_ms * 1e3, 1),
+                     "timed": "events in the timed region"},
+        "cpu_baseline": cpu,
+        "kernels": {"computed_rows_TFLOPs": round(2.0 * rows * N * H / (launch_ms * 1e-3) / 1e12, 1),
+                    "weight_bytes": wl.E * N * H, "kernel_hash": kernel_hash()},
     }
     print(json.dumps(res), flush=True)
 
