@@ -428,12 +428,16 @@ def bench_gemm(args):
         "config": {"workload": wl.name + "_gemm", "tokens": wl.T, "hidden": H, "experts": wl.E, "topk": wl.k,
                    "n": N, "pairs": pairs, "rows_computed": rows, "expert_alignment": wl.A},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 5000.0, "unit": "TFLOP/s",
-                     "frac": round(achieved / 5000.0, 4), "traffic": None, "kernel": "k_grouped_gemm_fp8",
+                     "frac": round(achieved / 5000.0, 4), "traffic": None,
+                     "kernel": "k_grouped_gemm_fp8_dma" if N % 256 == 0 and H // 128 <= 256 else "k_grouped_gemm_fp8",
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(launch_ms * 1e3, 1),
                      "timed": "events in the timed region"},
         "cpu_baseline": cpu,
         "kernels": {"computed_rows_TFLOPs": round(2.0 * rows * N * H / (launch_ms * 1e-3) / 1e12, 1),
-                    "weight_bytes": wl.E * N * H, "kernel_hash": kernel_hash()},
+                    "weight_bytes": wl.E * N * H,
+                    # the weights and A rows each cross HBM at least once
+                    "hbm_floor_us": round((wl.E * N * H + rows * (H + 4 * H // 128) + rows * N * 2) / 8e12 * 1e6, 1),
+                    "kernel_hash": kernel_hash()},
     }
     print(json.dumps(res), flush=True)
 

@@ -42,6 +42,7 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 constexpr int kTile = 128;
 constexpr int kLdsRow = kTile + 16;  // padded row stride (bytes)
 constexpr int kXcds = 8;
+constexpr int kMaxGemmKBlocks = 512;  // K / 128 limit of the DMA kernel (two column halves' scales in LDS)
 
 // Rows of expert e that the GEMM covers and the first tile's row.
 __device__ __forceinline__ void gemm_expert_tiles(const GemmArgs& a, int e, int& first_row, int& ntiles) {
@@ -210,8 +211,270 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_fp8(GemmArgs a) {
             }
 }
 
+// ---------------------------------------------------------------- 128 x 256 tiles, LDS DMA
+// For N % 256 == 0: a block of 8 waves computes a 128 x 256 tile (waves 2 x 4,
+// each a 64 x 64 piece as above). Operands move global -> LDS by DMA
+// (global_load_lds_dwordx4: lane i's 16 bytes land at the wave's LDS pointer
+// + 16 i, checked on MI355X), into a ring of kStages LDS stages, issued two
+// K blocks ahead, so up to 2 x 48 KiB per CU are in flight without staging
+// registers. LDS rows are not padded: 16-byte chunk c of row r is stored at
+// chunk position c ^ ((r / 2) mod 8) of its 128-byte row. A row covers half of
+// the 64 banks (rows of one parity the same half), so any 16 consecutive rows
+// read at one chunk hit all 64 banks exactly once. The row scales of a K block
+// come by 4-byte DMA (lane i -> + 4 i) into a ring of their own. Every wave
+// issues the same number of DMA loads per stage (waves 2..7 repeat a scale
+// load into a scratch LDS slot), and past the last K block the pipeline
+// re-issues the last stage's loads (the same bytes into the same buffer), so
+// the wait before each K block is one constant vmcnt.
+
+constexpr int kStages = 3;
+constexpr int kScaleStages = 4;  // row scales are read one K block later than the operands
+constexpr int kBN2 = 256;
+constexpr int kDmaPerStage = 2 + 4 + 1;  // A, B, scale loads per wave and stage
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+#define EP_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+
+// One global -> LDS DMA load per lane (16 or 4 bytes), written as inline
+// assembly: the compiler cannot tell which LDS bytes a DMA load writes, so
+// for the intrinsic it waits for every outstanding DMA load before any LDS
+// read, which would drain the prefetch ring each K block. Here the waits are
+// explicit (EP_WAIT_VMCNT + barrier before a stage is read). The source is a
+// wave-uniform base (scalar register pair) plus a 32-bit per-lane byte
+// offset, so that the per-lane part stays fixed over the K loop; `lds` is the
+// wave's LDS destination (uniform), lane i's data lands at lds + size * i.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// a pointer that is the same in every lane, moved to scalar registers
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[kStages][kTile * kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t s_b[kStages][kBN2 * kTile];
+    __shared__ __attribute__((aligned(16))) float s_sa[kScaleStages][kTile];
+    __shared__ __attribute__((aligned(16))) float s_dummy[64];
+    __shared__ float s_sb[kMaxGemmKBlocks];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nt_n = a.N / kBN2;
+
+    const int total = (int)gridDim.x;
+    const int q = total / kXcds, r = total % kXcds;
+    const int xcd = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
+    const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+
+    int e, n_tile, row0;
+    if (a.mode == EP_MODE_COMPACT) {
+        int lo = 0, hi = a.E;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((a.expert_off[mid] / kTile) * nt_n <= L) lo = mid;
+            else hi = mid - 1;
+        }
+        e = lo;
+        if (e >= a.E) return;
+        int first_row, ntiles;
+        gemm_expert_tiles(a, e, first_row, ntiles);
+        const int local = L - (first_row / kTile) * nt_n;
+        if (ntiles == 0 || local >= ntiles * nt_n) return;
+        n_tile = local / ntiles;
+        row0 = first_row + (local % ntiles) * kTile;
+    } else {
+        const int slots = a.C / kTile;
+        e = L / (slots * nt_n);
+        const int local = L % (slots * nt_n);
+        int first_row, ntiles;
+        gemm_expert_tiles(a, e, first_row, ntiles);
+        n_tile = local / slots;
+        const int m = local % slots;
+        if (m >= ntiles) return;
+        row0 = first_row + m * kTile;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    const int n0 = __builtin_amdgcn_readfirstlane(n_tile) * kBN2;
+    const int KB = a.K / kTile;
+
+    // weight-block scales of this column tile: all K blocks, once
+    const float* gsb = a.sb + ((int64_t)e * (a.N / kTile) + n0 / kTile) * KB;
+    const float* gsb2 = gsb + KB;  // the second 128-column half of the tile
+    for (int i = tid; i < 2 * KB; i += blockDim.x) s_sb[i] = i < KB ? gsb[i] : gsb2[i - KB];
+    EP_WAIT_VMCNT(0);
+    __syncthreads();
+
+    // DMA sources: tile bases (uniform) and per-lane offsets within K block 0;
+    // K block kb adds kb * 128 bytes (kb * 4 for the row scales) to the bases.
+    // Offsets fit 32 bits: at most 255 rows of K <= 32768 bytes.
+    const int sub = lane >> 3, ch = lane & 7;
+    const uint8_t* baseA = uniform_ptr(a.a + (int64_t)row0 * a.K);
+    const uint8_t* baseB = uniform_ptr(a.b + ((int64_t)e * a.N + n0) * a.K);
+    const float* baseS = uniform_ptr(a.sa + (int64_t)row0 * KB);
+    uint32_t offA[2], offB[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = (w * 2 + j) * 8 + sub;
+        offA[j] = (uint32_t)(m * a.K + ((ch ^ ((m >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = (w * 4 + j) * 8 + sub;
+        offB[j] = (uint32_t)(n * a.K + ((ch ^ ((n >> 1) & 7)) << 4));
+    }
+    const uint32_t offS = (uint32_t)(((w & 1) * 64 + lane) * KB * 4);  // scale row this lane moves
+    const uint32_t ldsA = lds_addr(&s_a[0][0]), ldsB = lds_addr(&s_b[0][0]);
+    const uint32_t ldsS = w < 2 ? lds_addr(&s_sa[0][0]) + w * 256 : lds_addr(s_dummy);
+    const uint32_t ldsS_step = w < 2 ? kTile * 4 : 0;
+
+    auto issue = [&](int kb) {
+        const int st = kb % kStages;
+        const uint8_t* ga = uniform_ptr(baseA + (int64_t)kb * kTile);
+        const uint8_t* gb = uniform_ptr(baseB + (int64_t)kb * kTile);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(ga, offA[j], ldsA + st * (kTile * kTile) + (w * 2 + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(gb, offB[j], ldsB + st * (kBN2 * kTile) + (w * 4 + j) * 1024);
+        dma4(uniform_ptr(baseS + kb), offS, ldsS + (kb % kScaleStages) * ldsS_step);
+    };
+    issue(0);
+    issue(min(1, KB - 1));
+    issue(min(2, KB - 1));
+
+    const int wm = w >> 2, wn = w & 3;
+    const int g = lane >> 5, r32 = lane & 31;
+    v16f_t acc[2][2], part[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[s][t][i] = 0.0f;
+
+    // LDS byte offsets of this lane's operand chunks within a stage, per K
+    // step (64 wide) and chunk of the pair; the second 32-row (column) piece
+    // is 32 rows = 4096 bytes further, with the same swizzle
+    uint32_t rdA[2][2], rdB[2][2];
+    {
+        const int ra = 64 * wm + r32, rb = 64 * wn + r32;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                rdA[ks][j] = 16 * swz(ra, 4 * ks + 2 * g + j);
+                rdB[ks][j] = 16 * swz(rb, 4 * ks + 2 * g + j);
+            }
+    }
+    // operands of one K step (64 wide) of one stage: A rows and B columns of
+    // this wave's two 32-row and two 32-column pieces
+    auto read_ops = [&](int st, int ks, v8i_t opa[2], v8i_t opb[2]) {
+        const uint8_t* la = &s_a[0][0] + st * (kTile * kTile);
+        const uint8_t* lb = &s_b[0][0] + st * (kBN2 * kTile);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const v4i_t a0 = *(const v4i_t*)(la + rdA[ks][0] + 4096 * s);
+            const v4i_t a1 = *(const v4i_t*)(la + rdA[ks][1] + 4096 * s);
+            const v4i_t b0 = *(const v4i_t*)(lb + rdB[ks][0] + 4096 * s);
+            const v4i_t b1 = *(const v4i_t*)(lb + rdB[ks][1] + 4096 * s);
+            opa[s] = (v8i_t){a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            opb[s] = (v8i_t){b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        }
+    };
+    // acc += part * (row scale * column scale) for the piece of K block kb
+    auto promote = [&](int kb, int s, int t) {
+        const float sbv = s_sb[(wn >> 1) * KB + kb];  // waves 0-1 and 2-3 of a row cover different halves
+        const float* sa = s_sa[kb % kScaleStages] + 64 * wm + 32 * s + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            acc[s][t][i] = __builtin_fmaf(part[s][t][i], sa[8 * (i >> 2) + (i & 3)] * sbv, acc[s][t][i]);
+    };
+
+    // Software pipeline over K blocks. On entry to K block kb both K steps'
+    // operands of stage kb are in registers and `part` holds K block kb - 1.
+    //  1. per 32 x 32 piece: promote its K block kb - 1 partial, then start
+    //     its first MFMA of K block kb (the FMAs overlap the MFMAs in flight);
+    //  2. barrier: every wave has finished reading stage kb (all its reads
+    //     were issued in the previous K block) and stage kb + 1 has landed;
+    //  3. DMA of stage kb + 3 into stage kb's buffer;
+    //  4. read stage kb + 1's first K step into the registers just consumed,
+    //     then the second MFMAs of K block kb, then stage kb + 1's second K
+    //     step. Past the last K block the reads hit a valid, unused stage.
+    // Row scales have a ring of 4: those of K block kb - 1 are read in step 1
+    // of K block kb, before the barrier after which stage kb + 3's land in
+    // that slot.
+    EP_WAIT_VMCNT(2 * kDmaPerStage);
+    __syncthreads();
+    asm volatile("" ::"v"(&s_a[0][0]), "v"(&s_b[0][0]), "v"(&s_sa[0][0]) : "memory");
+    v8i_t opa0[2], opb0[2], opa1[2], opb1[2];
+    read_ops(0, 0, opa0, opb0);
+    read_ops(0, 1, opa1, opb1);
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (kb > 0) promote(kb - 1, s, t);
+                v16f_t z;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opa0[s], opb0[t], z, 0, 0, 0, 127, 0, 127);
+            }
+        // keep the scheduler from moving the MFMAs and FMAs above past the
+        // barrier: they are meant to run while the wave waits at it
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): this wave's LDS reads are done
+        EP_WAIT_VMCNT(kDmaPerStage);              // this wave's loads of stage kb + 1 are done
+        __syncthreads();                          // ... and every other wave's
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"v"(&s_a[0][0]), "v"(&s_b[0][0]), "v"(&s_sa[0][0]) : "memory");
+        issue(min(kb + 3, KB - 1));
+        const int nxt = (kb + 1) % kStages;
+        read_ops(nxt, 0, opa0, opb0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opa1[s], opb1[t], part[s][t], 0, 0, 0,
+                                                                            127, 0, 127);
+        read_ops(nxt, 1, opa1, opb1);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) promote(KB - 1, s, t);
+    EP_WAIT_VMCNT(0);
+
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = row0 + 64 * wm + 32 * s + 8 * (i >> 2) + 4 * g + (i & 3);
+                const int col = n0 + 64 * wn + 32 * t + r32;
+                a.c[(int64_t)row * a.N + col] = (uint16_t)f32_to_bf16_rne(acc[s][t][i]);
+            }
+}
+
 hipError_t launch_grouped_gemm_fp8(const GemmArgs& a, int64_t rows_bound, hipStream_t stream) {
-    const int nt_n = a.N / kTile;
+    const bool wide = a.N % kBN2 == 0 && a.K / kTile <= kMaxGemmKBlocks / 2;
+    const int nt_n = a.N / (wide ? kBN2 : kTile);
     int64_t blocks;
     if (a.mode == EP_MODE_COMPACT)
         blocks = (rows_bound + kTile - 1) / kTile * nt_n;
@@ -219,7 +482,10 @@ hipError_t launch_grouped_gemm_fp8(const GemmArgs& a, int64_t rows_bound, hipStr
         blocks = (int64_t)a.E * (a.C / kTile) * nt_n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (wide)
+        hipLaunchKernelGGL(k_grouped_gemm_fp8_dma, dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_grouped_gemm_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
