@@ -32,8 +32,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch/combine effective GB/s + % of HBM peak, 8K tok×7168 top-8"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip", "ep_gemm.hip",
-                  "ep_device.h", "ep_layout_dev.h", "ep_dispatch_dev.h"]
+# the sources each step's kernels are built from (a profile taken with one
+# hash stays valid while those files are unchanged)
+KERNEL_SOURCES = {
+    "path": ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip", "ep_internal.h",
+             "ep_device.h", "ep_layout_dev.h", "ep_dispatch_dev.h"],
+    "gemm": ["ep_gemm.hip", "ep_internal.h", "ep_device.h"],
+}
 
 
 def parse():
@@ -58,9 +63,9 @@ def parse():
     return p.parse_args()
 
 
-def kernel_hash() -> str:
+def kernel_hash(step: str = "path") -> str:
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    for s in KERNEL_SOURCES[step]:
         with open(os.path.join(ROOT, "combine_ep_layout_10_amd", "csrc", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -437,7 +442,7 @@ def bench_gemm(args):
                     "weight_bytes": wl.E * N * H,
                     # the weights and A rows each cross HBM at least once
                     "hbm_floor_us": round((wl.E * N * H + rows * (H + 4 * H // 128) + rows * N * 2) / 8e12 * 1e6, 1),
-                    "kernel_hash": kernel_hash()},
+                    "kernel_hash": kernel_hash("gemm")},
     }
     print(json.dumps(res), flush=True)
 
