@@ -58,6 +58,8 @@ def parse():
                    help="capture one step in a HIP graph and time K replays (launch-bound shapes)")
     p.add_argument("--bound", action="store_true",
                    help="time steps issued through bound calls (arguments converted once)")
+    p.add_argument("--no-flush", action="store_true",
+                   help="skip the per-kernel pass with L2 and MALL flushed before each kernel")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip timing a plain 1 GiB device-to-device copy for reference")
     return p.parse_args()
@@ -280,6 +282,49 @@ def main():
                 "avg_launch_us": round(dom_ms * 1e3, 2),
                 "timed": "events in the timed region" if dom_live_ms is not None else "evented eager pass"}
 
+    flushed = None
+    if not args.no_flush and graph is None and bound is None:
+        # Cold-cache per-kernel times (not the timed region): before each of
+        # layout / dispatch / combine, a 512 MB buffer (larger than L2, 4 MB
+        # per XCD, plus the 256 MB MALL) is written and then read, so the
+        # caches hold only clean, unrelated lines (after a write alone the
+        # next kernel would also pay for writing back its dirty lines);
+        # medians over K steps.
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        sink = torch.empty((), dtype=torch.int64, device=dev)
+
+        def flush(v):
+            scratch.fill_(v)
+            torch.sum(scratch.view(torch.int32), dim=0, out=sink)
+
+        fl = []
+        for i in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            flush(i & 0x7F)
+            e[0].record(stream)
+            hf = ops.layout(cfg, idx, w, workspace=ws)
+            e[1].record(stream)
+            flush((i + 1) & 0x7F)
+            e[2].record(stream)
+            if fp8:
+                ops.dispatch(hf, x, dtype, recv=recv, recv_scales=rs)
+            else:
+                ops.dispatch(hf, x, dtype, recv=recv)
+            e[3].record(stream)
+            flush((i + 2) & 0x7F)
+            e[4].record(stream)
+            ops.combine(hf, y, w, out=out)
+            e[5].record(stream)
+            fl.append(e)
+        torch.cuda.synchronize()
+        med = [float(np.median([e[2 * j].elapsed_time(e[2 * j + 1]) for e in fl])) for j in range(3)]
+        flushed = {"layout_us": round(med[0] * 1e3, 2), "dispatch_us": round(med[1] * 1e3, 2),
+                   "combine_us": round(med[2] * 1e3, 2),
+                   "dispatch_frac": round(nbytes["dispatch"] / (med[1] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "combine_frac": round(nbytes["combine"] / (med[2] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "stat": "median of %d; 512 MB written and read before each kernel" % args.steps}
+        del scratch, sink
+
     copy_ceiling = None
     if not args.no_copy_ceiling:
         # Reference only: a plain 1 GiB device-to-device copy (read + write).
@@ -337,6 +382,7 @@ def main():
             "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
             "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
             "bytes": nbytes, "kernel_hash": khash,
+            "cold_cache": flushed,
             "copy_1GiB_GBps": copy_ceiling,
         },
     }

@@ -103,6 +103,62 @@ def test_random_layouts(T, E, k, A, D):
     _run_small(T, 64, E, k, A=A, D=D, seed=T + E)
 
 
+def _layout_every_table(mode, T, E, k, A, D, C, tables):
+    """One ep_layout launch per routing table, each into its own slice of one
+    workspace, one synchronisation, then every table's layout against the
+    oracle (which equals the O(P^2) brute-force definition on these same
+    tables: tests/test_oracle_layout.py)."""
+    n = len(tables)
+    log("every table: mode=%d T=%d E=%d k=%d A=%d D=%d C=%d, %d tables" % (mode, T, E, k, A, D, C, n))
+    cfg = ops.Config(max_tokens=T, hidden=128, num_experts=E, num_topk=k, num_dests=D,
+                     expert_alignment=A, capacity=C, mode=mode)
+    ws = -(-cfg.workspace_bytes() // 256) * 256
+    big = torch.empty(n * ws, dtype=torch.uint8, device="cuda")
+    idx_all = to_dev(np.ascontiguousarray(np.asarray(tables, np.int64)))
+    w = ((np.arange(T * k, dtype=np.float32) + 1) / 8).reshape(T, k)
+    w_dev = to_dev(w)
+    handles = [ops.layout(cfg, idx_all[i], w_dev, workspace=big[i * ws:(i + 1) * ws]) for i in range(n)]
+    torch.cuda.synchronize()
+    whole = big.cpu().numpy()
+    base = big.data_ptr()
+
+    def field(ptr, count, dt):
+        off = ptr - base
+        return whole[off: off + count * np.dtype(dt).itemsize].view(dt)
+
+    Rb = cfg.recv_rows_bound()
+    for i, (h, tab) in enumerate(zip(handles, tables)):
+        lay = oracle.layout(mode, T, E, k, A, D, C, np.asarray(tab, np.int64), w)
+        c = h.c
+        got = {"cnt": field(c.cnt, E, np.int32), "pad": field(c.pad, E, np.int32),
+               "expert_off": field(c.expert_off, E + 1, np.int32), "dest_off": field(c.dest_off, D + 1, np.int32),
+               "dest_tokens": field(c.dest_tokens, D, np.int32), "slot": field(c.slot, T * k, np.int32)}
+        for key, val in got.items():
+            assert np.array_equal(val, lay[key]), (i, tab, key)
+        assert int(field(c.err_flags, 1, np.int32)[0]) == lay["flags"], (i, tab)
+        rows = written_rows(lay)
+        assert np.array_equal(field(c.row_src, Rb, np.int32)[rows], lay["row_src"][rows]), (i, tab)
+        assert np.array_equal(field(c.row_w, Rb, np.float32)[rows].view(np.uint32),
+                              lay["row_w"][rows].view(np.uint32)), (i, tab)
+
+
+def test_every_tiny_routing_table():
+    """Every routing table with 4 tokens, 4 experts, top-2 distinct (12^4 =
+    20,736 tables; alignment 2, two destinations), bit-exact."""
+    import itertools
+    rows = list(itertools.permutations(range(4), 2))
+    _layout_every_table(oracle.MODE_COMPACT, 4, 4, 2, 2, 2, 0, list(itertools.product(rows, repeat=4)))
+
+
+def test_every_tiny_fixed_table():
+    """FIXED capacity 1 and 2: every table of 3 tokens, 3 experts, top-2 with
+    repeats allowed (9^3 tables), overflow flags included."""
+    import itertools
+    rows = list(itertools.product(range(3), repeat=2))
+    for C in (1, 2):
+        _layout_every_table(oracle.MODE_FIXED, 3, 3, 2, 1, 1, C, list(itertools.product(rows, repeat=3)))
+
+
 def test_masked_and_bad_ids():
     h, lay = _run_small(500, 128, 12, 4, A=3, D=4, seed=3, masked=0.2, bad=0.05, distinct=False)
     assert lay["flags"] == oracle.FLAG_BAD_ID and h.check() == oracle.FLAG_BAD_ID
