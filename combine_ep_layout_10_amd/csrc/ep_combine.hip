@@ -64,11 +64,8 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
                 }
             }
         }
-        uint4 o;
-        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-        o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-        o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+        const uint4 o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
         store_stream((uint4*)(a.out + (int64_t)t * a.H) + c, o);
     }
 }

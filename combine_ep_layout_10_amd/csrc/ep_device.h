@@ -21,6 +21,31 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two binary32 -> packed bfloat16 (a in the low half), round to nearest even,
+// by gfx950's v_cvt_pk_bf16_f32 (one instruction for both). Checked on
+// MI355X against f32_to_bf16_rne on every non-NaN binary32 pattern,
+// subnormals included: identical.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// fl(a / 448) for a >= 0 that is a bfloat16 value: the product with
+// c = fl(1/448) and one FMA correction (residual a - y * 448 is exact).
+// Checked in exact rational arithmetic on every finite non-negative bfloat16
+// value, subnormals included: equal to the IEEE quotient. Infinity passes
+// through (inf / 448 = inf).
+__device__ __forceinline__ float div448_bf16(float a) {
+    constexpr float c = 1.0f / 448.0f;
+    const float y = a * c;
+    const float e = __builtin_fmaf(-y, 448.0f, a);
+    const float s = __builtin_fmaf(e, c, y);
+    return a < __builtin_inff() ? s : a;
+}
+
 // ---------------------------------------------------------------- memory
 
 // Streaming (non-temporal) 16-byte accesses for data touched once: on gfx950

@@ -29,12 +29,8 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float f[8]) {
 }
 
 __device__ __forceinline__ uint4 pack_bf16x8(const float f[8]) {
-    uint4 o;
-    o.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
-    o.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
-    o.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
-    o.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
-    return o;
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
 }
 
 constexpr bool dispatch_is_fp8(int kind) {
@@ -94,28 +90,35 @@ __device__ __forceinline__ DispatchRaw dispatch_load(const DispatchArgs& a, int 
     return r;
 }
 
-// Quantises this lane's 16 values of a 1x128 block held by eight consecutive
-// lanes: amax over the block (DPP across the eight lanes), scale = amax /
-// 448, codes = E4M3(x / scale) rounded to nearest even, x / scale being the
-// IEEE binary32 quotient; an all-zero block gives scale 0 and zero codes.
-// Every lane of the wave must call it (inactive lanes hold zeros).
-//
-// The quotient is taken as q = y + (x - y*scale) * r with r = 1/scale and
-// y = x*r (one division per lane instead of 16; the residual is exact by
-// FMA), with x's sign copied back so that -0 stays -0. Checked exhaustively
-// on MI355X: for every pair of finite bf16 values |x| <= amax with
-// scale >= 2^-80, q equals the IEEE quotient wherever |x / scale| >= 2^-10
-// (below that every code is a signed zero and both agree). Smaller scales
-// (amax < 2^-71) take the IEEE division. The codes come from gfx950's
-// v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even), checked against an
-// integer round-to-nearest-even encoder on every binary32 of magnitude <=
-// 448.0001; quotients never exceed 448 * (1 + 2^-23) because |x| <= amax.
-__device__ __forceinline__ uint4 quantize16(const float f[16], float& scale_out) {
+// The amax of a 1x128 block held by eight consecutive lanes (16 values
+// each): this lane's maximum magnitude, then a DPP reduction across the
+// eight lanes. Every lane of the wave must call it (inactive lanes hold
+// zeros).
+__device__ __forceinline__ float block_amax16(const float f[16]) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = max8_dpp(amax);
-    const float scale = amax / 448.0f;
+    return max8_dpp(amax);
+}
+
+// Quantises this lane's 16 values of a 1x128 block whose amax (a bfloat16
+// value: the largest magnitude in the block) is given: scale = amax / 448,
+// codes = E4M3(x / scale) rounded to nearest even, x / scale being the IEEE
+// binary32 quotient; an all-zero block gives scale 0 and zero codes.
+//
+// scale = fl(amax / 448) by div448_bf16. The quotient is taken as
+// q = y + (x - y*scale) * r with r = 1/scale and y = x*r (one division per
+// lane instead of 16; the residual is exact by FMA), with x's sign copied
+// back so that -0 stays -0. Checked exhaustively on MI355X: for every pair of
+// finite bf16 values |x| <= amax with scale >= 2^-80, q equals the IEEE
+// quotient wherever |x / scale| >= 2^-10 (below that every code is a signed
+// zero and both agree). Smaller scales (amax < 2^-71) take the IEEE
+// division. The codes come from gfx950's v_cvt_pk_fp8_f32 (OCP E4M3, round
+// to nearest even), checked against an integer round-to-nearest-even
+// encoder on every binary32 of magnitude <= 448.0001; quotients never exceed
+// 448 * (1 + 2^-23) because |x| <= amax.
+__device__ __forceinline__ uint4 quantize16_amax(const float f[16], float amax, float& scale_out) {
+    const float scale = div448_bf16(amax);
     float q[16];
     if (scale >= 0x1p-80f) {
         const float r = 1.0f / scale;
@@ -138,6 +141,12 @@ __device__ __forceinline__ uint4 quantize16(const float f[16], float& scale_out)
     }
     scale_out = scale;
     return make_uint4(w4[0], w4[1], w4[2], w4[3]);
+}
+
+// The 1x128 block quantiser on 16 bf16 values per lane (every lane of the
+// wave must call it).
+__device__ __forceinline__ uint4 quantize16(const float f[16], float& scale_out) {
+    return quantize16_amax(f, block_amax16(f), scale_out);
 }
 
 // Turns loaded bytes into what is stored. FP8 quantise: the 1x128 block
@@ -169,21 +178,29 @@ __device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const Disp
     const int64_t row_out = kFp8 ? (int64_t)a.H : 2 * (int64_t)a.H;
     const int nb = a.H / 128;
     if (KIND == kDispatchFp8QuantWeighted) {
-        // Each pair's copy is bf16(w * x), quantised with its own scales. The
-        // pair loop is uniform (slots are broadcast), so every lane of the
-        // wave takes part in each block reduction; `act` guards the stores.
+        // Each pair's copy is bf16(w * x), quantised with its own scales.
+        // Rounding to binary32 and to bf16 is monotone and odd, so the
+        // block amax of bf16(w * x) is bf16(|w| * amax(x)) exactly: the
+        // block reduction over x runs once (every lane of the wave takes
+        // part; `act` guards only the stores), not once per pair.
         float f[16];
         unpack_bf16x8(d.v, f);
         unpack_bf16x8(d.v1, f + 8);
+        const float ax = block_amax16(f);
         for (int j = 0; j < a.k; ++j) {
             const int s = __builtin_amdgcn_readlane(my_s, j);
             if (s < 0) continue;
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
             float g[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) g[i] = bf16_to_f32(f32_to_bf16_rne(wj * f[i]));
+            for (int i = 0; i < 16; i += 2) {
+                const uint32_t p = pack_bf16x2(wj * f[i], wj * f[i + 1]);
+                g[i] = bf16_to_f32(p & 0xFFFFu);
+                g[i + 1] = __uint_as_float(p & 0xFFFF0000u);
+            }
+            const float ag = bf16_to_f32(pack_bf16x2(fabsf(wj) * ax, 0.0f) & 0xFFFFu);
             float scale;
-            const uint4 o = quantize16(g, scale);
+            const uint4 o = quantize16_amax(g, ag, scale);
             if (act) {
                 store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
                 if ((c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = scale;

@@ -473,6 +473,35 @@ def test_combine_backward_fp8_weighted_v3_shape():
     assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
 
 
+def test_combine_backward_fp8_weighted_all_patterns():
+    """Weighted FP8 combine_backward on every finite bf16 pattern (sorted by
+    magnitude, 128 to a block) under weights that reach the edges: signed
+    zeros, +-1, products that become binary32 subnormals or zero, and a
+    subnormal weight; every token sends to all 8 experts, each pair with its
+    own weight, bit-exact against the oracle."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = bits[np.isfinite((bits << 16).view(np.float32))].astype(np.uint16)
+    mag = np.abs((vals.astype(np.uint32) << 16).view(np.float32))
+    vals = vals[np.argsort(mag, kind="stable")]
+    H, k, E = 1024, 8, 8
+    T = -(-vals.size // H)
+    x = np.zeros(T * H, np.uint16)
+    x[:vals.size] = vals
+    x = x.reshape(T, H)
+    special = np.array([0.0, -0.0, 1.0, -1.0, 0.3, -0.70710678, 2.0 ** -100, -3.0 * 2.0 ** -130], np.float32)
+    w = np.stack([np.roll(special, t) for t in range(T)]).astype(np.float32)
+    idx = np.stack([np.roll(np.arange(E), t) for t in range(T)]).astype(np.int64)
+    log("weighted fp8 backward, all bf16 patterns: T=%d H=%d k=%d" % (T, H, k))
+    lay = oracle.layout(0, T, E, k, 1, 1, 0, idx, w)
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k)
+    h = ops.layout(cfg, to_dev(idx), to_dev(w))
+    q, sc = oracle.combine_backward_fp8(lay, x, k, w)
+    gq, gs = ops.combine_backward(h, to_dev_bf16(x), ops.FP8_QUANTIZE, to_dev(w))
+    rows = np.arange(lay["rows"])
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), sc[rows].view(np.uint32))
+
+
 def test_fp8_prequant_passthrough():
     rng = np.random.default_rng(15)
     T, H, E, k, A = 300, 512, 16, 4, 16
