@@ -159,6 +159,17 @@ def test_every_tiny_fixed_table():
         _layout_every_table(oracle.MODE_FIXED, 3, 3, 2, 1, 1, C, list(itertools.product(rows, repeat=3)))
 
 
+@pytest.mark.parametrize("T,H,E,k,A,D,dispatch", [
+    (64, 16384, 1024, 32, 2, 8, "fp8"),     # largest top-k and E; FP8 rows wider than 1024 lanes x 16 values
+    (40, 8200, 96, 32, 1, 4, "bf16"),       # 1025 vectors per row: every loop over a row wraps; 8200 % 128 != 0
+    (33, 8, 40, 32, 3, 5, "bf16"),          # one vector per row, k = 32 of 40 experts
+])
+def test_largest_topk_and_ragged_rows(T, H, E, k, A, D, dispatch):
+    _run_small(T, H, E, k, A=A, D=D, seed=T + H, dispatch=dispatch)
+    _run_small(T, H, E, k, A=A, D=D, seed=T + H + 1, dispatch=dispatch, forward=True, masked=0.2, bad=0.05,
+               distinct=False)
+
+
 def test_masked_and_bad_ids():
     h, lay = _run_small(500, 128, 12, 4, A=3, D=4, seed=3, masked=0.2, bad=0.05, distinct=False)
     assert lay["flags"] == oracle.FLAG_BAD_ID and h.check() == oracle.FLAG_BAD_ID
@@ -432,6 +443,7 @@ def _check_weight_grad(h, lay, g_bits, y_bits, k):
     (1, 8, 4, 1, 1, 0.0), (77, 264, 12, 3, 4, 0.2), (300, 2048, 32, 8, 16, 0.05),
     (64, 16384, 16, 6, 1, 0.0),      # two vectors per lane
     (40, 1024, 8, 12, 2, 0.1),       # k > 8: two groups of pairs
+    (24, 8200, 48, 32, 1, 0.1),      # largest top-k (four groups), 1025 vectors: the row loop wraps
 ])
 def test_combine_weight_grad(T, H, E, k, A, masked):
     log("weight grad T=%d H=%d E=%d k=%d" % (T, H, E, k))
