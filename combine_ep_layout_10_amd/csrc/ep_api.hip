@@ -394,7 +394,7 @@ ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_
         return fail(EP_ERR_INVALID_ARG, "a must be 16-byte aligned and a_scales non-NULL");
     if (b == nullptr || !aligned(b, 16) || b_scales == nullptr || !aligned(b_scales, 4))
         return fail(EP_ERR_INVALID_ARG, "b must be 16-byte aligned and b_scales non-NULL");
-    if (out == nullptr || !aligned(out, 4)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 4-byte aligned");
+    if (out == nullptr || !aligned(out, 16)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
     ep::GemmArgs g;
     g.a = (const uint8_t*)a;
     g.sa = a_scales;

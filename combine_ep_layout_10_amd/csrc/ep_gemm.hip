@@ -396,13 +396,19 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
             opb[s] = (v8i_t){b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         }
     };
-    // acc += part * (row scale * column scale) for the piece of K block kb
-    auto promote = [&](int kb, int s, int t) {
-        const float sbv = s_sb[(wn >> 1) * KB + kb];  // waves 0-1 and 2-3 of a row cover different halves
-        const float* sa = s_sa[kb % kScaleStages] + 64 * wm + 32 * s + 4 * g;
+    // The MFMAs take the B operand first, so each 32 x 32 piece comes out
+    // transposed: lane r32 holds one output row, element i of the 16 holds
+    // column 8 (i / 4) + 4 g + i % 4. The promotion factor (row scale x
+    // column-block scale) is then one value per lane and piece row: this
+    // wave's 64 columns lie in one 128-column scale block.
+    // acc += part * (row scale * column scale) for the pieces of K block kb
+    auto promote = [&](int kb, int s, int t, float f) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            acc[s][t][i] = __builtin_fmaf(part[s][t][i], sa[8 * (i >> 2) + (i & 3)] * sbv, acc[s][t][i]);
+        for (int i = 0; i < 16; ++i) acc[s][t][i] = __builtin_fmaf(part[s][t][i], f, acc[s][t][i]);
+    };
+    auto factor = [&](int kb, int s) {
+        const float sbv = s_sb[(wn >> 1) * KB + kb];  // waves 0-1 and 2-3 of a row cover different halves
+        return s_sa[kb % kScaleStages][64 * wm + 32 * s + r32] * sbv;
     };
 
     // Software pipeline over K blocks. On entry to K block kb both K steps'
@@ -425,15 +431,20 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
     read_ops(0, 0, opa0, opb0);
     read_ops(0, 1, opa1, opb1);
     for (int kb = 0; kb < KB; ++kb) {
+        float f[2] = {0.0f, 0.0f};
+        if (kb > 0) {
+            f[0] = factor(kb - 1, 0);
+            f[1] = factor(kb - 1, 1);
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                if (kb > 0) promote(kb - 1, s, t);
+                if (kb > 0) promote(kb - 1, s, t, f[s]);
                 v16f_t z;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opa0[s], opb0[t], z, 0, 0, 0, 127, 0, 127);
+                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opb0[t], opa0[s], z, 0, 0, 0, 127, 0, 127);
             }
         // keep the scheduler from moving the MFMAs and FMAs above past the
         // barrier: they are meant to run while the wave waits at it
@@ -450,25 +461,32 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opa1[s], opb1[t], part[s][t], 0, 0, 0,
+                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opb1[t], opa1[s], part[s][t], 0, 0, 0,
                                                                             127, 0, 127);
         read_ops(nxt, 1, opa1, opb1);
     }
+    {
+        const float f0 = factor(KB - 1, 0), f1 = factor(KB - 1, 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) promote(KB - 1, s, t);
+        for (int t = 0; t < 2; ++t) {
+            promote(KB - 1, 0, t, f0);
+            promote(KB - 1, 1, t, f1);
+        }
+    }
     EP_WAIT_VMCNT(0);
 
+    // epilogue: bf16, round to nearest even; four adjacent columns per store
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = row0 + 64 * wm + 32 * s + 8 * (i >> 2) + 4 * g + (i & 3);
-                const int col = n0 + 64 * wn + 32 * t + r32;
-                a.c[(int64_t)row * a.N + col] = (uint16_t)f32_to_bf16_rne(acc[s][t][i]);
+            for (int q = 0; q < 4; ++q) {
+                const int row = row0 + 64 * wm + 32 * s + r32;
+                const int col = n0 + 64 * wn + 32 * t + 8 * q + 4 * g;
+                const uint2 v = make_uint2(pack_bf16x2(acc[s][t][4 * q], acc[s][t][4 * q + 1]),
+                                           pack_bf16x2(acc[s][t][4 * q + 2], acc[s][t][4 * q + 3]));
+                *(uint2*)(a.c + (int64_t)row * a.N + col) = v;
             }
 }
 

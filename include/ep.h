@@ -266,9 +266,11 @@ ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const
  *              zero). FIXED: expert e's rows [e*C, e*C + ceil(pad[e]/128)*128)
  *              are written; those at or past e*C + pad[e] depend on whatever
  *              the receive rows hold. Other rows are not touched.
- * Requires hidden % 128 == 0, n % 128 == 0, and expert_alignment % 128 == 0
- * (COMPACT) or capacity % 128 == 0 (FIXED), so that every 128-row tile
- * belongs to one expert; otherwise EP_ERR_UNSUPPORTED. */
+ * a, b and out must be 16-byte aligned, the scale arrays 4-byte aligned
+ * (EP_ERR_INVALID_ARG otherwise). Requires hidden % 128 == 0, n % 128 == 0,
+ * and expert_alignment % 128 == 0 (COMPACT) or capacity % 128 == 0 (FIXED),
+ * so that every 128-row tile belongs to one expert; otherwise
+ * EP_ERR_UNSUPPORTED. */
 ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_scales, const void* b,
                               const float* b_scales, int32_t n, void* out, void* stream);
 
