@@ -403,6 +403,7 @@ ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_
     g.c = (uint16_t*)out;
     g.expert_off = h->expert_off;
     g.pad = h->pad;
+    g.cnt = h->cnt;
     g.E = c.num_experts;
     g.K = c.hidden;
     g.N = n;

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
     const int xcd = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
     const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
 
-    int e, n_tile, row0;
+    int e, n_tile, row0, live;  // live: rows of the tile that hold pairs (the rest are padding)
     if (a.mode == EP_MODE_COMPACT) {
         int lo = 0, hi = a.E;
         while (lo < hi) {
@@ -297,6 +297,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
         if (ntiles == 0 || local >= ntiles * nt_n) return;
         n_tile = local / ntiles;
         row0 = first_row + (local % ntiles) * kTile;
+        live = a.cnt[e] - (row0 - first_row);
     } else {
         const int slots = a.C / kTile;
         e = L / (slots * nt_n);
@@ -307,8 +308,10 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
         const int m = local % slots;
         if (m >= ntiles) return;
         row0 = first_row + m * kTile;
+        live = a.pad[e] - m * kTile;
     }
     e = __builtin_amdgcn_readfirstlane(e);
+    live = __builtin_amdgcn_readfirstlane(live);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     const int n0 = __builtin_amdgcn_readfirstlane(n_tile) * kBN2;
     const int KB = a.K / kTile;
@@ -359,6 +362,11 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
 
     const int wm = w >> 2, wn = w & 3;
     const int g = lane >> 5, r32 = lane & 31;
+    // 32-row pieces wholly past the expert's pairs are padding: their MFMAs
+    // and promotion are skipped (the wave still loads and waits with the
+    // block) and they are written as zeros, which is what zero padding rows
+    // give. The SIMD's other wave then has the MFMA unit to itself.
+    const bool live0 = 64 * wm < live, live1 = 64 * wm + 32 < live;
     v16f_t acc[2][2], part[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -440,6 +448,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                if (!(s == 0 ? live0 : live1)) continue;
                 if (kb > 0) promote(kb - 1, s, t, f[s]);
                 v16f_t z;
 #pragma unroll
@@ -461,16 +470,17 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_fp8_dma(GemmArgs a) {
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opb1[t], opa1[s], part[s][t], 0, 0, 0,
-                                                                            127, 0, 127);
+                if (s == 0 ? live0 : live1)
+                    part[s][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opb1[t], opa1[s], part[s][t], 0, 0, 0,
+                                                                                127, 0, 127);
         read_ops(nxt, 1, opa1, opb1);
     }
     {
         const float f0 = factor(KB - 1, 0), f1 = factor(KB - 1, 1);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            promote(KB - 1, 0, t, f0);
-            promote(KB - 1, 1, t, f1);
+            if (live0) promote(KB - 1, 0, t, f0);
+            if (live1) promote(KB - 1, 1, t, f1);
         }
     }
     EP_WAIT_VMCNT(0);

@@ -112,6 +112,7 @@ struct GemmArgs {
     uint16_t* c;
     const int32_t* expert_off;
     const int32_t* pad;
+    const int32_t* cnt;
     int E, K, N, mode, C;
 };
 

@@ -262,10 +262,12 @@ ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const
  *              hidden codes per output channel.
  *   b_scales   device binary32 [E, n/128, hidden/128]: 128x128 block scales.
  *   out        device bf16 [rows bound, n]. COMPACT: every row below
- *              expert_off[E] is written (padding rows too: zero codes give
- *              zero). FIXED: expert e's rows [e*C, e*C + ceil(pad[e]/128)*128)
- *              are written; those at or past e*C + pad[e] depend on whatever
- *              the receive rows hold. Other rows are not touched.
+ *              expert_off[E] is written; padding rows (past expert_off[e] +
+ *              cnt[e]) are zero when the receive padding rows are zero (the
+ *              default; unspecified under EP_FLAG_NO_ZERO_PAD). FIXED: expert
+ *              e's rows [e*C, e*C + ceil(pad[e]/128)*128) are written; those
+ *              at or past e*C + pad[e] are unspecified. Other rows are not
+ *              touched.
  * a, b and out must be 16-byte aligned, the scale arrays 4-byte aligned
  * (EP_ERR_INVALID_ARG otherwise). Requires hidden % 128 == 0, n % 128 == 0,
  * and expert_alignment % 128 == 0 (COMPACT) or capacity % 128 == 0 (FIXED),

@@ -92,10 +92,11 @@ def check(got_bits, ref_bits, bound):
     return err, lim
 
 
-def run_case(T, E, k, A, H, N, mode=0, C=0, seed=0, masked=0.0):
+def run_case(T, E, k, A, H, N, mode=0, C=0, seed=0, masked=0.0, idx=None):
     log("gemm case T=%d E=%d k=%d A=%d H=%d N=%d mode=%d C=%d" % (T, E, k, A, H, N, mode, C))
     rng = np.random.default_rng(seed)
-    idx = random_routing_table(rng, T, E, k, masked_frac=masked)
+    if idx is None:
+        idx = random_routing_table(rng, T, E, k, masked_frac=masked)
     x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A, capacity=C, mode=mode)
     h = ops.layout(cfg, to_dev(idx))
@@ -138,6 +139,18 @@ def run_case(T, E, k, A, H, N, mode=0, C=0, seed=0, masked=0.0):
 ])
 def test_grouped_gemm_compact(T, E, k, A, H, N):
     run_case(T, E, k, A, H, N, seed=T + E)
+
+
+def test_grouped_gemm_piece_boundaries():
+    """Experts holding 0, 1, 32, 33, 64, 65, 96, 97, 128 and 129 pairs: 32-row
+    pieces that are padding only are skipped and written as zeros, pieces
+    with at least one pair are computed (COMPACT and FIXED)."""
+    counts = [0, 1, 32, 33, 64, 65, 96, 97, 128, 129]
+    idx = np.concatenate([np.full(c, e, np.int64) for e, c in enumerate(counts)])
+    np.random.default_rng(3).shuffle(idx)
+    idx = idx[:, None]
+    run_case(idx.shape[0], len(counts), 1, 128, 256, 256, seed=11, idx=idx)
+    run_case(idx.shape[0], len(counts), 1, 1, 256, 256, mode=1, C=256, seed=12, idx=idx)
 
 
 def test_grouped_gemm_fixed():
