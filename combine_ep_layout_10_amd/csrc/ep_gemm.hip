@@ -8,7 +8,9 @@
 // sa [rows, K/128], B[e] the expert's E4M3 weights [N, K] with 128x128 block
 // scales sb[e] [N/128, K/128].
 //
-// Tiling (gfx950, wave64): a block of 4 waves computes a 128 x 128 tile of C;
+// Two kernels. For N % 256 == 0, k_grouped_gemm_fp8_dma (128 x 256 tiles fed
+// by LDS DMA; described with it below). For any N % 128, k_grouped_gemm_fp8:
+// (gfx950, wave64) a block of 4 waves computes a 128 x 128 tile of C;
 // each wave owns a 64 x 64 quarter as 2 x 2 MFMA tiles of 32 x 32. The K loop
 // runs over 128-wide scale blocks: the A and B tiles of one block (2 x 16 KiB)
 // are staged in LDS (rows padded to 144 bytes so the 16-byte operand reads of
