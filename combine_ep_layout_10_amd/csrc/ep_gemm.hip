@@ -1,6 +1,6 @@
 // FP8 grouped GEMM over the aligned expert-major layout: the consumer the
-// layout is built for (DeepEP README: per-expert received-token counts "for
-// GEMM", rows padded to expert_alignment; "New features": EPv2's new GEMM
+// layout is built for (DeepEP README: per-expert received-token counts meant for
+// the expert GEMM, rows padded to expert_alignment; "New features": EPv2's new GEMM
 // layout). For every row r of expert e and output channel n:
 //   C[r, n] = bf16( sum_kb sa[r, kb] * sb[e, n/128, kb]
 //                          * sum_{k in block kb} A[r, k] * B[e, n, k] )

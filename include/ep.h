@@ -248,7 +248,7 @@ ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const
                                  float* grad_topk_w, void* stream);
 
 /* FP8 grouped GEMM over the receive layout: the consumer the layout is built
- * for (README: per-expert received-token counts "for GEMM", rows padded to
+ * for (README: per-expert received-token counts meant for the expert GEMM, rows padded to
  * expert_alignment; "New features": EPv2's new GEMM layout). For every row r
  * of expert e and output channel c < n:
  *   out[r, c] = bf16( sum_kb a_scales[r, kb] * b_scales[e, c/128, kb]
@@ -278,7 +278,7 @@ ep_status ep_grouped_gemm_fp8(const ep_handle* h, const void* a, const float* a_
 
 /* Copies cnt and pad (host arrays of E, either may be NULL) and the row
  * total R (host, may be NULL) to the host. Synchronises the stream: this is
- * the README's "CPU sync" of a non-cached dispatch. */
+ * the README's CPU synchronisation of a non-cached dispatch. */
 ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, int64_t* rows,
                                 void* stream);
 

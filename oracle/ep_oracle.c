@@ -11,7 +11,7 @@
  *   - The problem: DeepEP README (community translation), opening paragraph
  *     and section "Interfaces and examples": dispatch routes each token to the
  *     experts of its top-k choice, combine reduces the expert outputs back.
- *   - Per-expert counts "for GEMM" and the expert_alignment argument:
+ *   - Per-expert counts meant for the expert GEMM and the expert_alignment argument:
  *     same README, "Example use in model training or inference prefilling"
  *     (dispatch_forward: handle.num_recv_tokens_per_expert_list,
  *     expert_alignment). The README's "New features" list names the new GEMM
@@ -502,7 +502,7 @@ static uint16_t ora_bf16_rne_f64(double v) {
 }
 
 /* The grouped GEMM the layout exists for (README: per-expert received-token
- * counts "for GEMM", rows padded to expert_alignment; "New features": the
+ * counts meant for the expert GEMM, rows padded to expert_alignment; "New features": the
  * new GEMM layout): rows of expert e, [row_begin[e], row_end[e]), times that
  * expert's weight matrix. A is the dispatched E4M3 codes [rows, K] with
  * 1x128 scales sa [rows, K/128]; expert e's weights are E4M3 codes
