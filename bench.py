@@ -89,6 +89,18 @@ def algorithmic_bytes(wl, R: int, P: int, dispatch: str) -> dict:
             "padding_rows": pad_rows, "pairs": P, "rows": R}
 
 
+def calib_copy(dev) -> None:
+    """Three plain 1 GiB device-to-device copies, the reference that
+    profile_summary scales FETCH_SIZE / WRITE_SIZE by."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def load_traffic(kernel: str, khash: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources."""
@@ -178,12 +190,7 @@ def main():
     dominant = "combine" if nbytes["combine"] >= nbytes["dispatch"] else "dispatch"
 
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        calib_copy(dev)
 
     graph = None
     if args.graph:
@@ -428,6 +435,8 @@ def bench_gemm(args):
     rows = R if wl.mode == 0 else int(sum(-(-p // 128) * 128 for p in pad))
     flops = 2.0 * pairs * N * H
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        calib_copy(dev)
     for _ in range(args.warmup):
         ops.grouped_gemm_fp8(h, q, s, b, sb, out=out)
     torch.cuda.synchronize()
@@ -471,6 +480,11 @@ def bench_gemm(args):
         cpu = {"value": round(2.0 * m * H / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
                "sample": "%d outputs (128-channel pieces of 64 random rows) of the same GEMM in %.1f s, "
                          "single-threaded C oracle in binary64" % (m, cpu_s)}
+    kname = "k_grouped_gemm_fp8_dma" if N % 256 == 0 and H // 128 <= 256 else "k_grouped_gemm_fp8"
+    # the least HBM traffic of one launch: weights and A rows (with scales)
+    # read once, the output rows written once
+    floor_bytes = wl.E * N * H + wl.E * (N // 128) * (H // 128) * 4 + rows * (H + 4 * H // 128) + rows * N * 2
+    khash = kernel_hash("gemm")
     res = {
         "metric": "FP8 grouped GEMM TFLOP/s on the receive layout", "value": round(tflops, 1), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -479,16 +493,15 @@ def bench_gemm(args):
         "config": {"workload": wl.name + "_gemm", "tokens": wl.T, "hidden": H, "experts": wl.E, "topk": wl.k,
                    "n": N, "pairs": pairs, "rows_computed": rows, "expert_alignment": wl.A},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 5000.0, "unit": "TFLOP/s",
-                     "frac": round(achieved / 5000.0, 4), "traffic": None,
-                     "kernel": "k_grouped_gemm_fp8_dma" if N % 256 == 0 and H // 128 <= 256 else "k_grouped_gemm_fp8",
+                     "frac": round(achieved / 5000.0, 4), "traffic": load_traffic(kname, khash),
+                     "kernel": kname,
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(launch_ms * 1e3, 1),
                      "timed": "events in the timed region"},
         "cpu_baseline": cpu,
         "kernels": {"computed_rows_TFLOPs": round(2.0 * rows * N * H / (launch_ms * 1e-3) / 1e12, 1),
-                    "weight_bytes": wl.E * N * H,
-                    # the weights and A rows each cross HBM at least once
-                    "hbm_floor_us": round((wl.E * N * H + rows * (H + 4 * H // 128) + rows * N * 2) / 8e12 * 1e6, 1),
-                    "kernel_hash": kernel_hash("gemm")},
+                    "weight_bytes": wl.E * N * H, "bytes": {"gemm": floor_bytes},
+                    "hbm_floor_us": round(floor_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6, 1),
+                    "kernel_hash": khash},
     }
     print(json.dumps(res), flush=True)
 

@@ -11,7 +11,9 @@ Two reports, both written as short text under profiles/:
            (the largest `__amd_rocclr_copyBuffer` dispatches, 2^30 bytes read
            and written): scale = 2^30 B / counter bytes for that copy. The
            scaled bytes of each kernel are set against the algorithmic bytes
-           `bench.py` reports for the same workload, and also stored in
+           `bench.py` reports for the same workload (for the grouped GEMM:
+           its HBM floor, weights and A read once, output written once), and
+           also stored in
            profiles/traffic.json, which `bench.py` reads for
            `roofline.traffic` while the kernel sources are unchanged.
 
@@ -121,7 +123,15 @@ def cmd_traffic(a) -> None:
     ws, wcopy = copy_scale(write)
     bench = load_bench(a.bench_json)
     khash = bench["kernels"]["kernel_hash"]
-    alg = {"k_dispatch": bench["kernels"]["bytes"]["dispatch"], "k_combine": bench["kernels"]["bytes"]["combine"]}
+    # algorithmic (or least) bytes per launch from the bench line: the path's
+    # dispatch and combine, or the grouped GEMM's HBM floor
+    by = bench["kernels"].get("bytes", {})
+    alg = {}
+    for key, names in (("dispatch", ["k_dispatch"]), ("combine", ["k_combine"]),
+                       ("gemm", ["k_grouped_gemm_fp8_dma", "k_grouped_gemm_fp8"])):
+        if key in by:
+            for n in names:
+                alg[n] = by[key]
     table = {}
     for name in sorted(set(fetch) | set(write)):
         if not name.startswith("ep::"):
@@ -152,6 +162,8 @@ def cmd_traffic(a) -> None:
         al = alg.get(key)
         ratio = "%.3f" % (nbytes / al) if al else "-"
         lines.append("| %s | %.1f | %.1f | %d | %s | %s |" % (name, f_kib, w_kib, nbytes, al if al else "-", ratio))
+        if key not in alg:
+            continue  # set-up kernels of this run (e.g. the dispatch before a GEMM): listed, not stored
         out_json[key] = {"bytes_per_launch": nbytes, "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
                          "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "kernel_hash": khash,
                          "workload": a.workload}
