@@ -74,6 +74,9 @@ def _stream() -> int:
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
+    if t.device.index != torch.cuda.current_device():
+        # kernels run on the current device's stream
+        raise ValueError("%s is on %s, not on the current device cuda:%d" % (name, t.device, torch.cuda.current_device()))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
