@@ -1,21 +1,28 @@
-"""Benchmark: MoE layout -> dispatch -> combine on one MI355X.
+"""Benchmark: MoE layout -> dispatch -> combine (and the backward duals) on one MI355X.
 
 One step = one pass of the whole path over one batch: ep_dispatch_forward
 (the layout — counts, offsets, stable slots — and the dispatch — FP8 E4M3
-1x128 quantise + copy for the V3 shape — in one call), then ep_combine
-(weighted BF16 reduction of the expert outputs). The expert computation
-between dispatch and combine is not part of this path; combine reads a
-seeded synthetic expert output of the receive layout.
+1x128 quantise + copy for the V3 shape — in one call), ep_combine (weighted
+BF16 reduction of the expert outputs), and, for the training-shaped
+workloads (aligned COMPACT layout), the backward duals on the cached
+handle: ep_combine_backward (a dispatch of the output gradient, each copy
+scaled by its pair weight, BF16) and ep_dispatch_backward (a combine of the
+receive-row gradients plus the gather of per-row weight gradients). The
+decode workload (FIXED capacity) is inference: forward only; so are
+--step forward, --graph and --bound. The expert computation between
+dispatch and combine is not part of this path; combine and the backward
+calls read seeded synthetic tensors of the receive layout.
 
 Inputs are seeded synthetic data resident in HBM before the timed region.
 Throughput is algorithmic bytes (the minimum each kernel must read and
-write) over time; `roofline` reports the dominant kernel against the
-MI355X HBM peak, timed with HIP events recorded around it inside the timed region, on the
-stream the kernels run on (--graph replays a captured step instead; the
-per-kernel times then come from an evented eager pass).
-`cpu_baseline` times the single-threaded CPU oracle on the same inputs.
+write) over time; `roofline` reports the kernel that moves the most bytes
+against the MI355X HBM peak, timed with HIP events recorded around it
+inside the timed region, on the stream the kernels run on (--graph replays a
+captured step instead; the per-kernel times then come from an evented eager
+pass). `cpu_baseline` times the single-threaded CPU oracle on the same inputs
+and the same work.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--graph | --bound]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--step path|forward] [--graph | --bound]
     python bench.py --step gemm [--gemm-n 4096]   # the FP8 grouped GEMM on the receive layout
 """
 from __future__ import annotations
@@ -47,8 +54,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="v3")
-    p.add_argument("--step", default="path", choices=["path", "gemm"],
-                   help="path: layout + dispatch + combine (the headline); gemm: the FP8 grouped GEMM consumer")
+    p.add_argument("--step", default="path", choices=["path", "forward", "gemm"],
+                   help="path: layout + dispatch + combine, plus the backward duals for COMPACT workloads "
+                        "(the headline); forward: without the backward duals; gemm: the FP8 grouped GEMM consumer")
     p.add_argument("--gemm-n", type=int, default=4096, help="output channels per expert for --step gemm")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -73,7 +81,7 @@ def kernel_hash(step: str = "path") -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, R: int, P: int, dispatch: str) -> dict:
+def algorithmic_bytes(wl, R: int, P: int, dispatch: str, train: bool = False) -> dict:
     """Minimum bytes each kernel must move (MB = 1e6 B in reports)."""
     T, H, k = wl.T, wl.H, wl.k
     nb = H // 128
@@ -85,8 +93,16 @@ def algorithmic_bytes(wl, R: int, P: int, dispatch: str) -> dict:
     layout = T * k * 8 + T * k * 4 + T * k * 4 + 2 * 4 * (R if wl.mode == 0 else P)
     dispatch_b = T * H * 2 + T * k * 4 + P * row_out + pad_rows * row_out
     combine = P * H * 2 + T * k * 4 + T * k * 4 + T * H * 2
-    return {"layout": layout, "dispatch": dispatch_b, "combine": combine,
-            "padding_rows": pad_rows, "pairs": P, "rows": R}
+    out = {"layout": layout, "dispatch": dispatch_b, "combine": combine,
+           "padding_rows": pad_rows, "pairs": P, "rows": R}
+    if train:
+        # combine_backward: grad_out, slots and pair weights in; every pair's
+        # weighted BF16 copy and the zero padding rows out
+        out["combine_backward"] = T * H * 2 + T * k * 4 + T * k * 4 + (P + pad_rows) * 2 * H
+        # dispatch_backward: the pairs' gradient rows and slots in, grad_x
+        # out, plus the per-row weight gradients gathered to [T, k]
+        out["dispatch_backward"] = P * H * 2 + T * k * 4 + T * H * 2 + P * 4 + T * k * 4
+    return out
 
 
 def calib_copy(dev) -> None:
@@ -102,8 +118,9 @@ def calib_copy(dev) -> None:
 
 
 def load_traffic(kernel: str, khash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources."""
+    """HBM bytes per launch of `kernel` (name with template arguments, e.g.
+    k_dispatch<2>) from committed rocprofv3 counter runs, if they were taken
+    on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -157,27 +174,56 @@ def main():
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        if fp8:
-            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
-        else:
-            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv)[0]
-        ops.combine(h, y, w, out=out)
-        return h
+    # training-shaped workloads also run the backward duals on the cached
+    # handle; decode (FIXED capacity) is inference, forward only
+    train = args.step == "path" and wl.mode == ops.MODE_COMPACT and not (args.graph or args.bound)
+    if train:
+        gen.manual_seed(5)
+        grad_out = torch.randn((wl.T, wl.H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        grad_recv = torch.randn((R_cap, wl.H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        grad_row_w = torch.randn((R_cap,), generator=gen, device=dev, dtype=torch.float32)
+        grad_y = torch.empty((R_cap, wl.H), dtype=torch.bfloat16, device=dev)
+        grad_x = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        grad_w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
 
-    def step_split(evs):
-        """The same work as separate layout / dispatch / combine calls, with
-        an event between them."""
-        evs[0].record(stream)
-        h = ops.layout(cfg, idx, w, workspace=ws)
-        evs[1].record(stream)
+    def do_dispatch(h):
         if fp8:
             ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs)
         else:
             ops.dispatch(h, x, dtype, recv=recv)
-        evs[2].record(stream)
-        ops.combine(h, y, w, out=out)
-        evs[3].record(stream)
+
+    # the calls after the layout, in step order, and the kernel each runs
+    calls = {"dispatch": do_dispatch, "combine": lambda h: ops.combine(h, y, w, out=out)}
+    kname = {"dispatch": "k_dispatch<2>" if fp8 else "k_dispatch<0>", "combine": "k_combine<true>"}
+    if train:
+        calls["combine_backward"] = lambda h: ops.combine_backward(h, grad_out, ops.BF16, w, grad_y=grad_y)
+        calls["dispatch_backward"] = lambda h: ops.dispatch_backward(h, grad_recv, grad_row_w, grad_x=grad_x,
+                                                                     grad_topk_w=grad_w)
+        kname["combine_backward"] = "k_dispatch<1>"
+        kname["dispatch_backward"] = "k_combine<false>"
+    names = list(calls)
+    after = names[1:]          # what follows the layout + dispatch call
+
+    def forward_head():
+        if fp8:
+            return ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
+        return ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv)[0]
+
+    def step():
+        h = forward_head()
+        for n in after:
+            calls[n](h)
+        return h
+
+    def step_split(evs):
+        """The same work as separate layout / dispatch / ... calls, with an
+        event between them."""
+        evs[0].record(stream)
+        h = ops.layout(cfg, idx, w, workspace=ws)
+        evs[1].record(stream)
+        for i, n in enumerate(names):
+            calls[n](h)
+            evs[i + 2].record(stream)
 
     h = step()
     cnt, pad, R = h.read_counts()
@@ -185,9 +231,9 @@ def main():
     if flags:
         raise RuntimeError("layout raised error flags %d on a valid workload" % flags)
     P = int(cnt.sum()) if wl.mode == 0 else int(pad.sum())
-    nbytes = algorithmic_bytes(wl, R, P, wl.dispatch)
-    step_bytes = nbytes["layout"] + nbytes["dispatch"] + nbytes["combine"]
-    dominant = "combine" if nbytes["combine"] >= nbytes["dispatch"] else "dispatch"
+    nbytes = algorithmic_bytes(wl, R, P, wl.dispatch, train)
+    step_bytes = nbytes["layout"] + sum(nbytes[n] for n in names)
+    dominant = max(names, key=lambda n: nbytes[n])
 
     if args.calib_copy:
         calib_copy(dev)
@@ -240,33 +286,37 @@ def main():
             bound[1]()
             continue
         e0, e1 = dom_ev[i]
-        if dominant == "combine":
-            h = ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
-            e0.record(stream)
-            ops.combine(h, y, w, out=out)
-            e1.record(stream)
-        else:
+        if dominant == "dispatch":
             h = ops.layout(cfg, idx, w, workspace=ws)
             e0.record(stream)
-            ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs) if fp8 else ops.dispatch(h, x, dtype, recv=recv)
+            do_dispatch(h)
             e1.record(stream)
-            ops.combine(h, y, w, out=out)
+            for n in after:
+                calls[n](h)
+        else:
+            h = forward_head()
+            for n in after:
+                if n == dominant:
+                    e0.record(stream)
+                    calls[n](h)
+                    e1.record(stream)
+                else:
+                    calls[n](h)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     live = graph is None and bound is None
     dom_live_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_ev])) if live else None
-    # Per-kernel durations: K more steps as separate layout / dispatch /
-    # combine calls with events between them (not part of the timed region).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Per-kernel durations: K more steps as separate layout / dispatch / ...
+    # calls with events between them (not part of the timed region).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 2)] for _ in range(args.steps)]
     for i in range(args.steps):
         step_split(evs[i])
     torch.cuda.synchronize()
     lay_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dis_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    com_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    gpu_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
-    # dispatch_forward as one unit (one launch for small batches)
+    k_ms = {n: float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in evs])) for i, n in enumerate(names)}
+    gpu_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
+    # the step with dispatch_forward as one unit (one launch for small batches)
     fw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1 in fw:
         e0.record(stream)
@@ -277,25 +327,23 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     khash = kernel_hash()
-    com_gbps = nbytes["combine"] / (com_ms * 1e-3) / 1e9
-    dis_gbps = nbytes["dispatch"] / (dis_ms * 1e-3) / 1e9
-    dom_ms = dom_live_ms if dom_live_ms is not None else (com_ms if dominant == "combine" else dis_ms)
+    gbps = {n: nbytes[n] / (k_ms[n] * 1e-3) / 1e9 for n in names}
+    dom_ms = dom_live_ms if dom_live_ms is not None else k_ms[dominant]
     dom_gbps = nbytes[dominant] / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic("k_combine" if dominant == "combine" else "k_dispatch", khash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "k_combine<true>" if dominant == "combine" else "k_dispatch",
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(kname[dominant], khash),
+                "kernel": kname[dominant], "call": dominant,
                 "algorithmic_bytes_per_launch": nbytes[dominant],
                 "avg_launch_us": round(dom_ms * 1e3, 2),
                 "timed": "events in the timed region" if dom_live_ms is not None else "evented eager pass"}
 
     flushed = None
     if not args.no_flush and graph is None and bound is None:
-        # Cold-cache per-kernel times (not the timed region): before each of
-        # layout / dispatch / combine, a 512 MB buffer (larger than L2, 4 MB
-        # per XCD, plus the 256 MB MALL) is written and then read, so the
-        # caches hold only clean, unrelated lines (after a write alone the
-        # next kernel would also pay for writing back its dirty lines);
+        # Cold-cache per-kernel times (not the timed region): before the
+        # layout and before each later call, a 512 MB buffer (larger than L2,
+        # 4 MB per XCD, plus the 256 MB MALL) is written and then read, so
+        # the caches hold only clean, unrelated lines (after a write alone
+        # the next kernel would also pay for writing back its dirty lines);
         # medians over K steps.
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         sink = torch.empty((), dtype=torch.int64, device=dev)
@@ -306,30 +354,24 @@ def main():
 
         fl = []
         for i in range(args.steps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (len(names) + 1))]
             flush(i & 0x7F)
             e[0].record(stream)
             hf = ops.layout(cfg, idx, w, workspace=ws)
             e[1].record(stream)
-            flush((i + 1) & 0x7F)
-            e[2].record(stream)
-            if fp8:
-                ops.dispatch(hf, x, dtype, recv=recv, recv_scales=rs)
-            else:
-                ops.dispatch(hf, x, dtype, recv=recv)
-            e[3].record(stream)
-            flush((i + 2) & 0x7F)
-            e[4].record(stream)
-            ops.combine(hf, y, w, out=out)
-            e[5].record(stream)
+            for j, n in enumerate(names):
+                flush((i + j + 1) & 0x7F)
+                e[2 * j + 2].record(stream)
+                calls[n](hf)
+                e[2 * j + 3].record(stream)
             fl.append(e)
         torch.cuda.synchronize()
-        med = [float(np.median([e[2 * j].elapsed_time(e[2 * j + 1]) for e in fl])) for j in range(3)]
-        flushed = {"layout_us": round(med[0] * 1e3, 2), "dispatch_us": round(med[1] * 1e3, 2),
-                   "combine_us": round(med[2] * 1e3, 2),
-                   "dispatch_frac": round(nbytes["dispatch"] / (med[1] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                   "combine_frac": round(nbytes["combine"] / (med[2] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                   "stat": "median of %d; 512 MB written and read before each kernel" % args.steps}
+        med = [float(np.median([e[2 * j].elapsed_time(e[2 * j + 1]) for e in fl])) for j in range(len(names) + 1)]
+        flushed = {"layout_us": round(med[0] * 1e3, 2)}
+        for j, n in enumerate(names):
+            flushed[n + "_us"] = round(med[j + 1] * 1e3, 2)
+            flushed[n + "_frac"] = round(nbytes[n] / (med[j + 1] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        flushed["stat"] = "median of %d; 512 MB written and read before each kernel" % args.steps
         del scratch, sink
 
     copy_ceiling = None
@@ -355,6 +397,10 @@ def main():
         import oracle
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        if train:
+            go_h = grad_out.view(torch.int16).cpu().numpy().view(np.uint16)
+            gr_h = grad_recv.view(torch.int16).cpu().numpy().view(np.uint16)
+            grw_h = grad_row_w.cpu().numpy()
         times = []
         budget_end = time.perf_counter() + args.cpu_budget_s
         while not times or (len(times) < 3 and time.perf_counter() < budget_end):
@@ -365,33 +411,42 @@ def main():
             else:
                 oracle.dispatch_bf16(lay, x_h, wl.k)
             oracle.combine(lay, y_h, wl.k, w_h)
+            if train:
+                oracle.combine_backward_bf16(lay, go_h, wl.k, w_h)
+                oracle.dispatch_backward(lay, gr_h, wl.k, grw_h)
             times.append(time.perf_counter() - c0)
             print("[bench] oracle step %.2f s" % times[-1], file=sys.stderr, flush=True)
         cpu_s = float(np.median(times))
         cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "the full %s step (layout + %s dispatch + combine) on the same inputs, median of %d "
-                         "runs of %.2f s; single-threaded C oracle" % (wl.name, wl.dispatch, len(times), cpu_s)}
+               "sample": "the full %s step (layout + %s dispatch + combine%s) on the same inputs, median of %d "
+                         "runs of %.2f s; single-threaded C oracle"
+                         % (wl.name, wl.dispatch, " + combine_backward + dispatch_backward" if train else "",
+                            len(times), cpu_s)}
 
+    kernels = {"layout_us": round(lay_ms * 1e3, 2)}
+    for n in names:
+        kernels[n + "_us"] = round(k_ms[n] * 1e3, 2)
+    kernels.update({"gpu_step_us": round(gpu_ms * 1e3, 2), "step_with_dispatch_forward_us": round(step_ev_ms * 1e3, 2),
+                    "graph": bool(args.graph), "bound": bool(args.bound)})
+    for n in names:
+        kernels[n + "_GBps"] = round(gbps[n], 1)
+        kernels[n + "_frac"] = round(gbps[n] / HBM_PEAK_GBPS, 4)
+    kernels.update({"bytes": nbytes, "kernel_bytes": {kname[n]: nbytes[n] for n in names}, "kernel_hash": khash,
+                    "cold_cache": flushed, "copy_1GiB_GBps": copy_ceiling})
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "launch": "graph" if args.graph else ("bound" if args.bound else "eager"), "tokens": wl.T, "hidden": wl.H, "experts": wl.E, "topk": wl.k,
+        "config": {"workload": wl.name, "step": "forward+backward" if train else "forward",
+                   "launch": "graph" if args.graph else ("bound" if args.bound else "eager"), "tokens": wl.T,
+                   "hidden": wl.H, "experts": wl.E, "topk": wl.k,
                    "expert_alignment": wl.A, "dests": wl.D, "mode": "fixed" if wl.mode else "compact",
-                   "dispatch": "fp8_e4m3_1x128" if fp8 else "bf16", "combine": "bf16", "routing": wl.routing},
+                   "dispatch": "fp8_e4m3_1x128" if fp8 else "bf16", "combine": "bf16",
+                   "backward": "bf16 weighted combine_backward, dispatch_backward with weight-grad gather"
+                               if train else None, "routing": wl.routing},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernels": {
-            "layout_us": round(lay_ms * 1e3, 2), "dispatch_us": round(dis_ms * 1e3, 2),
-            "combine_us": round(com_ms * 1e3, 2), "gpu_step_us": round(gpu_ms * 1e3, 2),
-            "dispatch_forward_plus_combine_us": round(step_ev_ms * 1e3, 2), "graph": bool(args.graph),
-            "bound": bool(args.bound),
-            "dispatch_GBps": round(dis_gbps, 1), "combine_GBps": round(com_gbps, 1),
-            "dispatch_frac": round(dis_gbps / HBM_PEAK_GBPS, 4), "combine_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
-            "bytes": nbytes, "kernel_hash": khash,
-            "cold_cache": flushed,
-            "copy_1GiB_GBps": copy_ceiling,
-        },
+        "kernels": kernels,
     }
     print(json.dumps(res), flush=True)
 
@@ -499,7 +554,7 @@ def bench_gemm(args):
                      "timed": "events in the timed region"},
         "cpu_baseline": cpu,
         "kernels": {"computed_rows_TFLOPs": round(2.0 * rows * N * H / (launch_ms * 1e-3) / 1e12, 1),
-                    "weight_bytes": wl.E * N * H, "bytes": {"gemm": floor_bytes},
+                    "weight_bytes": wl.E * N * H, "kernel_bytes": {kname: floor_bytes},
                     "hbm_floor_us": round(floor_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6, 1),
                     "kernel_hash": khash},
     }

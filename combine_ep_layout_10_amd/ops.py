@@ -273,13 +273,20 @@ def combine(h: Handle, y: torch.Tensor, topk_w: Optional[torch.Tensor] = None, o
     return out if row_vals is None else (out, out_vals)
 
 
-def dispatch_backward(h: Handle, grad_recv: torch.Tensor, grad_row_w: Optional[torch.Tensor] = None):
-    """README dispatch_backward: returns grad_x (and grad_topk_w)."""
+def dispatch_backward(h: Handle, grad_recv: torch.Tensor, grad_row_w: Optional[torch.Tensor] = None,
+                      grad_x: Optional[torch.Tensor] = None, grad_topk_w: Optional[torch.Tensor] = None):
+    """README dispatch_backward: returns grad_x (and grad_topk_w when
+    grad_row_w is given), into the given buffers or new ones."""
     T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
     _need(grad_recv, (h.cfg.recv_rows_bound(), H), "grad_recv")
     _need(grad_row_w, (h.cfg.recv_rows_bound(),), "grad_row_w")
-    gx = torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
-    gw = None if grad_row_w is None else torch.empty((T, k), dtype=torch.float32, device=grad_recv.device)
+    gx = grad_x if grad_x is not None else torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
+    _need(gx, (T, H), "grad_x")
+    gw = None
+    if grad_row_w is not None:
+        gw = grad_topk_w if grad_topk_w is not None else torch.empty((T, k), dtype=torch.float32,
+                                                                     device=grad_recv.device)
+        _need(gw, (T, k), "grad_topk_w")
     F.ep_dispatch_backward(h.c, _dev(grad_recv, "grad_recv", torch.bfloat16),
                            _opt(grad_row_w, "grad_row_w", torch.float32), _dev(gx, "grad_x", torch.bfloat16),
                            _opt(gw, "grad_topk_w", torch.float32), _stream())

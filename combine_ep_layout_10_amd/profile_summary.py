@@ -50,12 +50,13 @@ def short_name(full: str) -> str:
     return n
 
 
-def base_key(name: str) -> str:
-    """Key in traffic.json: the kernel name without namespace or template
-    arguments (`ep::k_dispatch<2>` -> `k_dispatch`)."""
+def kernel_key(name: str) -> str:
+    """Key in traffic.json: the kernel name without the namespace, template
+    arguments kept (`ep::k_dispatch<2>` -> `k_dispatch<2>`): one kernel
+    template serves several calls (the FP8 dispatch and the weighted BF16
+    combine_backward are both k_dispatch)."""
     n = short_name(name)
-    n = n.split("::")[-1] if "<" not in n else n[:n.index("<")].split("::")[-1]
-    return n
+    return n[len("ep::"):] if n.startswith("ep::") else n
 
 
 def read_stats(path: str):
@@ -123,15 +124,9 @@ def cmd_traffic(a) -> None:
     ws, wcopy = copy_scale(write)
     bench = load_bench(a.bench_json)
     khash = bench["kernels"]["kernel_hash"]
-    # algorithmic (or least) bytes per launch from the bench line: the path's
-    # dispatch and combine, or the grouped GEMM's HBM floor
-    by = bench["kernels"].get("bytes", {})
-    alg = {}
-    for key, names in (("dispatch", ["k_dispatch"]), ("combine", ["k_combine"]),
-                       ("gemm", ["k_grouped_gemm_fp8_dma", "k_grouped_gemm_fp8"])):
-        if key in by:
-            for n in names:
-                alg[n] = by[key]
+    # algorithmic (or least) bytes per launch of each kernel the bench line
+    # measures: the path's calls, or the grouped GEMM's HBM floor
+    alg = dict(bench["kernels"].get("kernel_bytes", {}))
     table = {}
     for name in sorted(set(fetch) | set(write)):
         if not name.startswith("ep::"):
@@ -158,7 +153,7 @@ def cmd_traffic(a) -> None:
         with open(a.json) as f:
             out_json = json.load(f)
     for name, (f_kib, w_kib, nbytes) in table.items():
-        key = base_key(name)
+        key = kernel_key(name)
         al = alg.get(key)
         ratio = "%.3f" % (nbytes / al) if al else "-"
         lines.append("| %s | %.1f | %.1f | %d | %s | %s |" % (name, f_kib, w_kib, nbytes, al if al else "-", ratio))
