@@ -66,7 +66,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         }
         const uint4 o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-        store_stream((uint4*)(a.out + (int64_t)t * a.H) + c, o);
+        store_row_stream(a.out + (int64_t)t * a.H, 2u * (uint32_t)a.H, 16u * c, o);
     }
 }
 

@@ -65,6 +65,25 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
 
 __device__ __forceinline__ void store_stream_f32(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
+// Streaming 16-byte store into one row through a buffer resource, with the
+// cache policy sc0 sc1 nt (LLVM's GLC | SLC | SCC bits, read by gfx950 as
+// sc0, nt and sc1). Measured on MI355X on the dispatch's pattern (a 14 KiB
+// row read, then written to 8 rows): 6.36 TB/s of total traffic against
+// 5.83 TB/s with plain non-temporal global stores. `row` must be the same in
+// every lane (it becomes the resource's base, in scalar registers); stores at
+// or past `row_bytes` are dropped by the hardware. The resource's last word
+// selects 32-bit data (0x00020000); with 0 the stores are dropped (checked).
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kCpolStream = 1 | 2 | 16;
+
+typedef unsigned int u32x4b_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_row_stream(void* row, uint32_t row_bytes, uint32_t off, uint4 v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)row_bytes, kBufferFlags);
+    const u32x4b_t x = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kCpolStream);
+}
+
 // ---------------------------------------------------------------- wave ops
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

@@ -48,8 +48,8 @@ __device__ __forceinline__ void dispatch_zero_rows(const DispatchArgs& a, int r0
     const int nvec = (int)(row_out / 16);
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     for (int r = r0; r < r1; ++r) {
-        uint4* dst = (uint4*)((char*)a.recv + (int64_t)r * row_out);
-        for (int c = tid; c < nvec; c += nthreads) store_stream(dst + c, z);
+        char* dst = (char*)a.recv + (int64_t)r * row_out;
+        for (int c = tid; c < nvec; c += nthreads) store_row_stream(dst, (uint32_t)row_out, 16u * c, z);
         if (kFp8)
             for (int b = tid; b < nb; b += nthreads) a.recv_scales[(int64_t)r * nb + b] = 0.0f;
     }
@@ -202,7 +202,7 @@ __device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const Disp
             float scale;
             const uint4 o = quantize16_amax(g, ag, scale);
             if (act) {
-                store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
+                store_row_stream((char*)a.recv + (int64_t)s * row_out, (uint32_t)row_out, 16u * c, o);
                 if ((c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = scale;
             }
         }
@@ -222,7 +222,7 @@ __device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const Disp
             for (int i = 0; i < 8; ++i) g[i] = wj * f[i];
             o = pack_bf16x8(g);
         }
-        store_stream((uint4*)((char*)a.recv + (int64_t)s * row_out) + c, o);
+        store_row_stream((char*)a.recv + (int64_t)s * row_out, (uint32_t)row_out, 16u * c, o);
         if (kFp8 && (c & 7) == 0) a.recv_scales[(int64_t)s * nb + (c >> 3)] = d.scale;
     }
 }
