@@ -1,0 +1,109 @@
+"""Host-side measurement logic (no GPU): the algorithmic byte counts the
+benchmark divides by, and the rocprofv3 summaries (kernel-name parsing,
+copy-calibrated traffic scaling, which kernels traffic.json records)."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+from combine_ep_layout_10_amd import profile_summary as ps
+from ep_workloads import WORKLOADS
+
+
+def test_v3_algorithmic_bytes_by_hand():
+    """V3: 8192 tokens x 7168, top-8, 65,536 pairs, 80,768 aligned rows
+    (15,232 of padding); every term written out by hand."""
+    wl = WORKLOADS["v3"]
+    T, H, k, P, R = 8192, 7168, 8, 65536, 80768
+    b = bench.algorithmic_bytes(wl, R, P, "fp8", train=True)
+    row_fp8 = H + 4 * (H // 128)                              # codes + 56 scales
+    assert b["dispatch"] == T * H * 2 + T * k * 4 + R * row_fp8
+    assert b["dispatch"] == 714_739_712
+    assert b["combine"] == P * H * 2 + 2 * T * k * 4 + T * H * 2 == 1_057_488_896
+    assert b["combine_backward"] == T * H * 2 + 2 * T * k * 4 + R * 2 * H == 1_275_854_848
+    assert b["dispatch_backward"] == P * H * 2 + T * k * 4 + T * H * 2 + P * 4 + T * k * 4
+    assert b["padding_rows"] == R - P == 15_232
+    fwd = bench.algorithmic_bytes(wl, R, P, "fp8")
+    assert "combine_backward" not in fwd and fwd["combine"] == b["combine"]
+
+
+def test_fixed_mode_has_no_padding_bytes():
+    wl = WORKLOADS["decode"]
+    b = bench.algorithmic_bytes(wl, 256 * 128, 1024, "fp8")
+    assert b["padding_rows"] == 0
+    assert b["dispatch"] == 128 * 7168 * 2 + 128 * 8 * 4 + 1024 * (7168 + 4 * 56)
+
+
+def test_kernel_names():
+    full = "void ep::k_combine<true>(ep::CombineArgs)"
+    assert ps.short_name(full) == "ep::k_combine<true>"
+    assert ps.kernel_key(full) == "k_combine<true>"
+    assert ps.kernel_key("void ep::k_layout_dispatch_small<1, 2>(ep::LayoutArgs, ep::DispatchArgs)") == \
+        "k_layout_dispatch_small<1, 2>"
+    assert ps.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for name, grid, val in rows:
+            w.writerow([name, grid, counter, val])
+
+
+def test_traffic_scaling_and_recorded_kernels(tmp_path):
+    """The 1 GiB copy fixes the scale (FETCH reads half the bytes here, WRITE
+    all of them); only kernels the bench line names are stored, under
+    their template-qualified names and the bench's source hash."""
+    copy = "__amd_rocclr_copyBuffer"
+    disp = "void ep::k_dispatch<1>(ep::DispatchArgs)"
+    setup = "void ep::k_layout_count(ep::LayoutArgs)"
+    gib_kib = (1 << 30) / 1024
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 4096, 1.0), (copy, 1 << 20, gib_kib / 2),
+                                                     (disp, 99, 1000.0), (disp, 99, 1002.0), (setup, 8, 3.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1 << 20, gib_kib), (disp, 99, 5000.0), (setup, 8, 1.0)])
+    line = {"kernels": {"kernel_hash": "abc", "kernel_bytes": {"k_dispatch<1>": 7_000_000}}}
+    (tmp_path / "b.log").write_text("[bench] noise\n" + json.dumps(line) + "\n")
+    out_json = tmp_path / "traffic.json"
+    out_json.write_text(json.dumps({"k_combine<true>": {"bytes_per_launch": 1, "kernel_hash": "old"}}))
+    ps.main(["traffic", "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
+             "--workload", "w", "--command-fetch", "cf", "--command-write", "cw",
+             "--bench-json", str(tmp_path / "b.log"), "--out", str(tmp_path / "t.md"), "--json", str(out_json)])
+    t = json.loads(out_json.read_text())
+    assert set(t) == {"k_combine<true>", "k_dispatch<1>"}        # set-up kernel listed in the table, not stored
+    e = t["k_dispatch<1>"]
+    assert e["kernel_hash"] == "abc" and e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["bytes_per_launch"] == round((1001.0 * 2 + 5000.0) * 1024)
+    assert t["k_combine<true>"]["kernel_hash"] == "old"          # other entries are kept
+    md = (tmp_path / "t.md").read_text()
+    assert "ep::k_layout_count" in md and "| 7000000 |" in md
+
+
+def test_traffic_needs_the_copy(tmp_path):
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [("void ep::k_combine<true>(ep::CombineArgs)", 1, 1.0)])
+    with pytest.raises(SystemExit):
+        ps.copy_scale(ps.read_counter(str(tmp_path / "f.csv"), "FETCH_SIZE"))
+
+
+def test_trace_summary(tmp_path):
+    p = tmp_path / "s.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow(["void ep::k_combine<true>(ep::CombineArgs)", 4, 800000, 200000.0, 50, 190000, 210000, 1])
+        w.writerow(["void at::native::fill(int)", 9, 90, 10.0, 1, 9, 11, 0])
+    rows = ps.read_stats(str(p))
+    assert rows[0] == ("ep::k_combine<true>", 4, 200.0, 190.0, 210.0)
+    ps.main(["trace", str(p), "--workload", "w", "--command", "c", "--out", str(tmp_path / "o.md")])
+    md = (tmp_path / "o.md").read_text()
+    assert "| ep::k_combine<true> | 4 | 200.00 | 190.00 | 210.00 |" in md
+    assert "at::native" not in md                               # only this library's kernels
+
+
+def test_kernel_hash_tracks_step_sources():
+    assert bench.kernel_hash("path") != bench.kernel_hash("gemm")
+    for step, files in bench.KERNEL_SOURCES.items():
+        for f in files:
+            assert os.path.exists(os.path.join(bench.ROOT, "combine_ep_layout_10_amd", "csrc", f)), (step, f)
