@@ -54,9 +54,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="v3")
-    p.add_argument("--step", default="path", choices=["path", "forward", "gemm"],
+    p.add_argument("--step", default="path", choices=["path", "forward", "gemm", "weight_grad", "fp8_backward"],
                    help="path: layout + dispatch + combine, plus the backward duals for COMPACT workloads "
-                        "(the headline); forward: without the backward duals; gemm: the FP8 grouped GEMM consumer")
+                        "(the headline); forward: without the backward duals; gemm: the FP8 grouped GEMM consumer; "
+                        "weight_grad / fp8_backward: one training call on the cached layout (the routing-weight "
+                        "gradient, the weighted FP8 combine_backward)")
     p.add_argument("--gemm-n", type=int, default=4096, help="output channels per expert for --step gemm")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -146,6 +148,8 @@ def main():
 
     if args.step == "gemm":
         return bench_gemm(args)
+    if args.step in ("weight_grad", "fp8_backward"):
+        return bench_call(args)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -447,6 +451,114 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_call(args):
+    """One training call on the cached layout of a workload, K launches:
+    ep_combine_weight_grad (grad_topk_w[t, j] = <grad_out[t], y[slot]>) or
+    ep_combine_backward with FP8 output and pair weights (each pair's copy
+    bf16(w * grad_out) quantised 1x128 with its own scales). Algorithmic
+    bytes as for the path's calls; roofline against the HBM peak."""
+    import numpy as np
+    import torch
+    from ep_workloads import WORKLOADS, draw_routing, draw_weights, _streams
+    from combine_ep_layout_10_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    if wl.mode != ops.MODE_COMPACT or wl.H % 128:
+        print("--step %s needs a COMPACT workload with hidden %% 128 == 0" % args.step, file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    sx, sr, sl, so, sy = _streams(0)
+    idx_h = draw_routing(wl, sr)
+    w_h = draw_weights(wl, sl)
+    cfg = ops.Config(max_tokens=wl.T, hidden=wl.H, num_experts=wl.E, num_topk=wl.k, num_dests=wl.D,
+                     expert_alignment=wl.A, capacity=wl.C, mode=wl.mode, idx_bits=64)
+    R_cap = cfg.recv_rows_bound()
+    idx = torch.from_numpy(idx_h).to(dev)
+    w = torch.from_numpy(w_h).to(dev)
+    h = ops.layout(cfg, idx, w)
+    cnt, pad, R = h.read_counts()
+    P = int(cnt.sum())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    grad_out = torch.randn((wl.T, wl.H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    T, H, k = wl.T, wl.H, wl.k
+    if args.step == "weight_grad":
+        y = torch.randn((R_cap, H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+        def call():
+            ops.combine_weight_grad(h, grad_out, y, gw)
+        # grad_out and the pairs' rows of y in, slots in, one float per pair out
+        nbytes = T * H * 2 + P * H * 2 + T * k * 4 + T * k * 4
+        kname, what = "k_weight_grad", "ep_combine_weight_grad"
+    else:
+        gq = torch.empty((R_cap, H), dtype=torch.uint8, device=dev)
+        gs = torch.empty((R_cap, H // 128), dtype=torch.float32, device=dev)
+
+        def call():
+            ops.combine_backward(h, grad_out, ops.FP8_QUANTIZE, w, grad_y=gq, grad_y_scales=gs)
+        # grad_out, slots and weights in; every row (pairs and zero padding)
+        # with its 1x128 scales out
+        nbytes = T * H * 2 + T * k * 4 + T * k * 4 + R * (H + 4 * (H // 128))
+        kname, what = "k_dispatch<4>", "ep_combine_backward (FP8, weighted)"
+    stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        calib_copy(dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    khash = kernel_hash()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, idx_h, w_h)
+        go_h = grad_out.view(torch.int16).cpu().numpy().view(np.uint16)
+        if args.step == "weight_grad":
+            y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)
+            run = lambda: oracle.combine_weight_grad(lay, go_h, y_h, wl.k)
+        else:
+            run = lambda: oracle.combine_backward_fp8(lay, go_h, wl.k, w_h)
+        times = []
+        budget_end = time.perf_counter() + args.cpu_budget_s
+        while not times or (len(times) < 3 and time.perf_counter() < budget_end):
+            c0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - c0)
+        cpu_s = float(np.median(times))
+        cpu = {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the same %s call on the same inputs, median of %d runs of %.2f s; single-threaded "
+                         "C oracle" % (what, len(times), cpu_s)}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name + "_" + args.step, "call": what, "tokens": T, "hidden": H,
+                   "experts": wl.E, "topk": k, "expert_alignment": wl.A, "routing": wl.routing},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(kname, khash),
+                     "kernel": kname, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(launch_ms * 1e3, 2), "timed": "events in the timed region"},
+        "cpu_baseline": cpu,
+        "kernels": {"kernel_bytes": {kname: nbytes}, "kernel_hash": khash, "pairs": P, "rows": R},
     }
     print(json.dumps(res), flush=True)
 
