@@ -170,6 +170,48 @@ def test_grouped_gemm_masked_and_unsupported():
                              torch.zeros((4, 1, 2), device="cuda"))
 
 
+def test_grouped_gemm_no_zero_pad_and_empty():
+    """EP_FLAG_NO_ZERO_PAD: padding rows keep whatever the receive buffer held
+    (here E4M3 NaN codes and NaN scales); every row holding a pair is still
+    exact within the bound, since an output row depends on its own A row
+    only. An empty batch leaves the output untouched."""
+    T, E, k, A, H, N = 300, 6, 2, 128, 256, 256
+    rng = np.random.default_rng(21)
+    idx = random_routing_table(rng, T, E, k)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, expert_alignment=A,
+                     flags=ops.FLAG_NO_ZERO_PAD)
+    R = cfg.recv_rows_bound()
+    h = ops.layout(cfg, to_dev(idx))
+    q = torch.full((R, H), 0x7F, dtype=torch.uint8, device="cuda")
+    s = torch.full((R, H // 128), float("nan"), dtype=torch.float32, device="cuda")
+    ops.dispatch(h, to_dev_bf16(x), ops.FP8_QUANTIZE, recv=q, recv_scales=s)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    b = random_codes(gen, (E, N, H))
+    sb = torch.rand((E, N // 128, H // 128), device="cuda", generator=gen) * 1e-2 + 1e-3
+    out = torch.full((R, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ops.grouped_gemm_fp8(h, q, s, b, sb, out=out)
+    torch.cuda.synchronize()
+    qh, sh, bh, sbh = host(q), host(s), host(b), host(sb)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    cnt, pad, _ = h.read_counts()
+    off = host(h.expert_off)
+    rb, re_ = off[:-1], off[:-1] + cnt
+    ref = oracle.grouped_gemm_fp8(rb, re_, qh, sh, bh, sbh)
+    for e in range(E):
+        rows = np.arange(rb[e], re_[e])
+        if rows.size:
+            bound, _ = gemm_bound(qh, sh, bh, sbh, rows, e, np.arange(N))
+            check(got[rows], ref[rows], bound)
+    # empty batch: nothing is written
+    h0 = ops.layout(cfg, torch.zeros((0, k), dtype=torch.int64, device="cuda"))
+    out0 = torch.full((R, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ops.grouped_gemm_fp8(h0, q, s, b, sb, out=out0)
+    torch.cuda.synchronize()
+    assert bool((out0.view(torch.int16) == -1).all())
+
+
 def test_grouped_gemm_v3_sampled():
     """The V3 receive layout (8192 x 7168, 256 experts, top-8, 80K rows) times
     a 7168 -> 4096 expert matrix per expert (7.5 GB of E4M3 weights): 512
