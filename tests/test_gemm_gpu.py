@@ -136,6 +136,10 @@ def run_case(T, E, k, A, H, N, mode=0, C=0, seed=0, masked=0.0, idx=None):
     (300, 6, 2, 128, 512, 256),
     (97, 5, 3, 256, 256, 384),     # alignment 256: two tiles per padded group
     (40, 16, 2, 128, 128, 128),    # many experts with no rows
+    (60, 4, 2, 128, 128, 256),     # 256-column kernel, one K block: its prologue re-issues the only stage
+    (60, 4, 2, 128, 256, 512),     # two K blocks, two column tiles
+    (24, 2, 1, 128, 32768, 256),   # the 256-column kernel's largest K (256 blocks of 128)
+    (24, 2, 1, 128, 32896, 256),   # one K block more: the 128-column kernel takes it
 ])
 def test_grouped_gemm_compact(T, E, k, A, H, N):
     run_case(T, E, k, A, H, N, seed=T + E)
