@@ -105,7 +105,7 @@ ep_status check_handle(const ep_handle* h) {
 }
 
 // Checks a dispatch and fills its kernel arguments; enqueues nothing.
-ep_status prepare_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales,
+ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales,
                            const float* pair_w, void* recv, float* recv_scales, ep::DispatchArgs* out, int* kind) {
     ep_status s = check_handle(h);
     if (s != EP_OK) return s;
@@ -151,7 +151,7 @@ ep_status prepare_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, co
     return EP_OK;
 }
 
-ep_status do_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales, const float* pair_w,
+ep_status do_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales, const float* pair_w,
                       void* recv, float* recv_scales, hipStream_t stream) {
     ep::DispatchArgs a;
     int kind = 0;
@@ -304,7 +304,7 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
 }
 
 ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
-                              void* workspace, size_t workspace_bytes, ep_dtype dtype, const void* x,
+                              void* workspace, size_t workspace_bytes, int32_t dtype, const void* x,
                               const float* x_scales, void* recv, float* recv_scales, ep_handle* out, void* stream) {
     ep_handle h;
     ep::LayoutArgs la;
@@ -333,7 +333,7 @@ ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const vo
     return EP_OK;
 }
 
-ep_status ep_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales, void* recv,
+ep_status ep_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales, void* recv,
                       float* recv_scales, void* stream) {
     return do_dispatch(h, dtype, x, x_scales, nullptr, recv, recv_scales, (hipStream_t)stream);
 }
@@ -348,7 +348,7 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
     return do_combine(h, grad_recv, nullptr, grad_x, grad_row_w, grad_topk_w, (hipStream_t)stream);
 }
 
-ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* grad_out, const float* topk_w,
+ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* grad_out, const float* topk_w,
                               void* grad_y, float* grad_y_scales, void* stream) {
     if (topk_w != nullptr && dtype == EP_FP8_PREQUANT)
         return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward needs EP_BF16 or EP_FP8_QUANTIZE");
@@ -441,7 +441,7 @@ ep_status ep_handle_check(const ep_handle* h, uint32_t* flags, void* stream) {
     return EP_OK;
 }
 
-const char* ep_status_string(ep_status s) {
+const char* ep_status_string(int32_t s) {
     switch (s) {
         case EP_OK: return "EP_OK";
         case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";

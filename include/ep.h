@@ -77,7 +77,10 @@ typedef enum { EP_MODE_COMPACT = 0, EP_MODE_FIXED = 1 } ep_mode;
  *   [rows, hidden], recv_scales is binary32 [rows, hidden/128] row-major.
  * EP_FP8_PREQUANT: x is already E4M3FN [T, hidden] with x_scales binary32
  *   [T, hidden/128] (the README's (data, scale_factors) tuple); codes and
- *   scales are copied bitwise. */
+ *   scales are copied bitwise.
+ * Entry points take the payload type as an int32_t holding one of these
+ * values (any other value is EP_ERR_INVALID_ARG), so that a caller's
+ * out-of-range value is an error rather than an invalid enum. */
 typedef enum { EP_BF16 = 0, EP_FP8_QUANTIZE = 1, EP_FP8_PREQUANT = 2 } ep_dtype;
 
 /* ep_config.flags */
@@ -180,7 +183,7 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
  * kernel. Never synchronises. */
 ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
                               const float* topk_w, void* workspace, size_t workspace_bytes,
-                              ep_dtype dtype, const void* x, const float* x_scales, void* recv,
+                              int32_t dtype, const void* x, const float* x_scales, void* recv,
                               float* recv_scales, ep_handle* out, void* stream);
 
 /* Dispatch on an existing handle (README dispatch_forward, or dispatch with a
@@ -194,7 +197,7 @@ ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const vo
  *              expert_off[E] are not touched.
  *   recv_scales device [rows bound, hidden/128] binary32 for the FP8 types
  *              (padding rows get 0), else NULL. */
-ep_status ep_dispatch(const ep_handle* h, ep_dtype dtype, const void* x, const float* x_scales,
+ep_status ep_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales,
                       void* recv, float* recv_scales, void* stream);
 
 /* Combine (README combine_forward): for every token t and channel c,
@@ -225,7 +228,7 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
  * with EP_FP8_QUANTIZE that BF16 copy is then quantised per 1x128 block as
  * ep_dispatch quantises x, each pair with its own scales. EP_FP8_PREQUANT
  * with topk_w returns EP_ERR_UNSUPPORTED. */
-ep_status ep_combine_backward(const ep_handle* h, ep_dtype dtype, const void* grad_out,
+ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* grad_out,
                               const float* topk_w, void* grad_y, float* grad_y_scales,
                               void* stream);
 
@@ -286,8 +289,9 @@ ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, 
  * Synchronises the stream. */
 ep_status ep_handle_check(const ep_handle* h, uint32_t* flags, void* stream);
 
-/* Static text for a status code. */
-const char* ep_status_string(ep_status s);
+/* Static text for a status code (an ep_status value; any other value
+ * gives "EP_ERR_UNKNOWN"). */
+const char* ep_status_string(int32_t s);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* ep_last_error_message(void);

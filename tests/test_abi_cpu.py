@@ -166,3 +166,29 @@ def test_dispatch_forward_argument_errors():
     assert f(ctypes.byref(c), 4, fake, None, fake, need, F.EP_BF16, fake, None, fake, None, None,
              None) == F.EP_ERR_INVALID_ARG                                     # out NULL
     assert "out handle" in F.last_error_message()
+
+
+def test_grouped_gemm_argument_errors():
+    """Every shape and pointer rule of ep_grouped_gemm_fp8 is checked on the
+    host before the launch (no call below reaches the GPU)."""
+    lib = F.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)                          # 8-byte, not 16-byte, aligned
+    g = lib.ep_grouped_gemm_fp8
+    h = fake_handle(expert_alignment=128)
+    assert g(None, fake, fake, fake, fake, 256, fake, None) == F.EP_ERR_INVALID_ARG
+    for n in (0, -128, 64, 200):
+        assert g(ctypes.byref(h), fake, fake, fake, fake, n, fake, None) == F.EP_ERR_INVALID_ARG, n
+    assert g(ctypes.byref(fake_handle(hidden=200, expert_alignment=128)), fake, fake, fake, fake, 256, fake,
+             None) == F.EP_ERR_UNSUPPORTED                                  # hidden % 128
+    assert g(ctypes.byref(fake_handle(expert_alignment=64)), fake, fake, fake, fake, 256, fake,
+             None) == F.EP_ERR_UNSUPPORTED                                  # a tile would span two experts
+    assert g(ctypes.byref(fake_handle(mode=F.EP_MODE_FIXED, capacity=96)), fake, fake, fake, fake, 256, fake,
+             None) == F.EP_ERR_UNSUPPORTED
+    for args in ((None, fake, fake, fake), (odd, fake, fake, fake), (fake, None, fake, fake),
+                 (fake, ctypes.c_void_p((1 << 20) + 2), fake, fake), (fake, fake, None, fake),
+                 (fake, fake, odd, fake), (fake, fake, fake, None)):
+        assert g(ctypes.byref(h), *args, 256, fake, None) == F.EP_ERR_INVALID_ARG, args
+    assert g(ctypes.byref(h), fake, fake, fake, fake, 256, None, None) == F.EP_ERR_INVALID_ARG
+    assert g(ctypes.byref(h), fake, fake, fake, fake, 256, odd, None) == F.EP_ERR_INVALID_ARG
+    assert "16-byte" in F.last_error_message()
