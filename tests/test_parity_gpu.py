@@ -562,7 +562,8 @@ def test_fp8_codec_all_bf16_patterns():
     bm = np.abs((blocks.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
     for factor in (1.0, 1.5, 3.0, 2.0 ** 9, 2.0 ** 20):
         top = float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])   # largest finite bf16
-        amax = f32_to_bf16_bits(np.minimum(np.maximum(bm, 2.0 ** -100) * factor, top).astype(np.float32))
+        amax = f32_to_bf16_bits(np.minimum(np.maximum(bm.astype(np.float64), 2.0 ** -100) * factor, top)
+                                .astype(np.float32))
         x = np.concatenate([amax[:, None], blocks], axis=1)            # [nblk, 128]
         T = nblk
         H = 128
