@@ -78,16 +78,16 @@ _SIGNATURES = {
     "ep_layout": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
                                  ctypes.POINTER(ep_handle), _P]),
     "ep_dispatch_forward": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
-                                           ctypes.c_int, _P, _P, _P, _P, ctypes.POINTER(ep_handle), _P]),
-    "ep_dispatch": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int, _P, _P, _P, _P, _P]),
+                                           ctypes.c_int32, _P, _P, _P, _P, ctypes.POINTER(ep_handle), _P]),
+    "ep_dispatch": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P]),
     "ep_combine": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),
-    "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int, _P, _P, _P, _P, _P]),
+    "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P]),
     "ep_combine_weight_grad": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_handle_check": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P]),
-    "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ep_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "ep_last_error_message": (ctypes.c_char_p, []),
 }
 
