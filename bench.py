@@ -378,22 +378,29 @@ def main():
         flushed["stat"] = "median of %d; 512 MB written and read before each kernel" % args.steps
         del scratch, sink
 
-    copy_ceiling = None
+    copy_ceiling = fill_ceiling = None
     if not args.no_copy_ceiling:
-        # Reference only: a plain 1 GiB device-to-device copy (read + write).
+        # Reference only, torch's own kernels on 1 GiB: a device-to-device copy
+        # (read + write) and a fill (a pure write stream, the pattern of the
+        # write-dominated calls).
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            b.copy_(a)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        copy_ceiling = round(2 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+
+        def med_ms(fn):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts))
+
+        copy_ceiling = round(2 * (1 << 30) / (med_ms(lambda: b.copy_(a)) * 1e-3) / 1e9, 1)
+        fill_ceiling = round((1 << 30) / (med_ms(lambda: b.fill_(0)) * 1e-3) / 1e9, 1)
         del a, b
 
     cpu = None
@@ -436,7 +443,8 @@ def main():
         kernels[n + "_GBps"] = round(gbps[n], 1)
         kernels[n + "_frac"] = round(gbps[n] / HBM_PEAK_GBPS, 4)
     kernels.update({"bytes": nbytes, "kernel_bytes": {kname[n]: nbytes[n] for n in names}, "kernel_hash": khash,
-                    "cold_cache": flushed, "copy_1GiB_GBps": copy_ceiling})
+                    "cold_cache": flushed, "copy_1GiB_GBps": copy_ceiling,
+                    "fill_1GiB_GBps": fill_ceiling})
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
