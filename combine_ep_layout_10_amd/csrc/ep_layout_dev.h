@@ -163,10 +163,14 @@ __device__ __forceinline__ void small_layout(const LayoutArgs& a, int32_t* lds, 
     }
     L.over = __syncthreads_or(over);
     L.padv = padv;
-    int total;
-    const int excl = block_exclusive_scan(padv, tmp, &total);
-    if (tid < a.E) L.s_off[tid] = a.mode == EP_MODE_COMPACT ? excl : tid * a.C;
-    if (tid == 0) L.s_off[a.E] = a.mode == EP_MODE_COMPACT ? total : a.E * a.C;
+    if (a.mode == EP_MODE_COMPACT) {  // uniform: the scan's barriers are reached by all or none
+        int total;
+        const int excl = block_exclusive_scan(padv, tmp, &total);
+        if (tid < a.E) L.s_off[tid] = excl;
+        if (tid == 0) L.s_off[a.E] = total;
+    } else if (tid <= a.E) {
+        L.s_off[tid] = tid * a.C;  // FIXED: expert e owns [e*C, e*C + C) whatever the counts
+    }
     __syncthreads();
 }
 
