@@ -29,17 +29,18 @@ __device__ __forceinline__ int load_group(const LayoutArgs& a, int64_t base, boo
 }
 
 // Pair (t, j) is counted for destination dd when no earlier pair of token t
-// goes to dd. Earlier pairs in this group of 64 are read from their lanes;
-// those in an earlier group are loaded.
+// goes to dd. Earlier pairs in this group of 64 are the lanes below this one
+// that hold the same token: a peer mask over the bits of dd (ballots, as for
+// the expert ids) restricted to them; pairs in an earlier group are loaded.
 __device__ __forceinline__ bool first_in_dest(const LayoutArgs& a, int64_t base, int dd, bool v) {
     const int lane = lane_id();
     const int64_t p = base + lane;
     const int j = (int)(p % a.k);
-    bool first = v;
-    for (int m = 1; m < a.k; ++m) {
-        const int other = __shfl(dd, (lane - m) & (kWave - 1), kWave);
-        if (m <= j && lane >= m && other == dd) first = false;
-    }
+    const int dbits = a.D > 1 ? 32 - __clz(a.D - 1) : 0;
+    const uint64_t same = match_peers(dd, v, dbits);
+    const int below = j < lane ? j : lane;  // same-token lanes below this one in the group
+    const uint64_t tok_below = lanes_below(lane) & ~lanes_below(lane - below);
+    bool first = v && (same & tok_below) == 0;
     if (v && j > lane) {
         for (int jj = 0; jj < j - lane; ++jj) {
             bool v2, b2;
