@@ -139,9 +139,8 @@ ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, con
     a.k = c.num_topk;
     a.E = c.num_experts;
     a.zero_pad = (c.mode == EP_MODE_COMPACT && !(c.flags & EP_FLAG_NO_ZERO_PAD)) ? 1 : 0;
-    a.pad_blocks_per_expert = a.zero_pad ? (c.expert_alignment - 1 + ep::kPadRowsPerBlock - 1) / ep::kPadRowsPerBlock : 0;
-    a.npad_blocks = a.pad_blocks_per_expert * c.num_experts;
-    if (a.pad_blocks_per_expert == 0) a.pad_blocks_per_expert = 1;  // never divided by when npad_blocks == 0
+    a.pad_rows_max = a.zero_pad ? c.expert_alignment - 1 : 0;
+    ep::set_pad_blocks(a, ep::kPadRowsPerBlock);  // the single-launch path sets its own
     if (dtype == EP_BF16)
         *kind = pair_w ? ep::kDispatchBf16Weighted : ep::kDispatchBf16;
     else if (dtype == EP_FP8_QUANTIZE)

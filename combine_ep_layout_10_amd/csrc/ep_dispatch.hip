@@ -15,11 +15,11 @@ namespace ep {
 template <int KIND>
 __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
     if ((int)blockIdx.x < a.npad_blocks) {
-        // zero-fill up to kPadRowsPerBlock padding rows of one expert
+        // zero-fill up to pad_rows_per_block padding rows of one expert
         const int e = blockIdx.x / a.pad_blocks_per_expert;
         const int part = blockIdx.x % a.pad_blocks_per_expert;
-        const int r0 = a.expert_off[e] + a.cnt[e] + part * kPadRowsPerBlock;
-        const int r1 = min(r0 + kPadRowsPerBlock, a.expert_off[e] + a.pad[e]);
+        const int r0 = a.expert_off[e] + a.cnt[e] + part * a.pad_rows_per_block;
+        const int r1 = min(r0 + a.pad_rows_per_block, a.expert_off[e] + a.pad[e]);
         dispatch_zero_rows<KIND>(a, r0, r1);
         return;
     }
@@ -41,8 +41,10 @@ hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream) 
     int threads = ((nvec + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
     if (threads < 64) threads = 64;
-    const int grid = a.npad_blocks + a.T;
-    if (grid == 0) return hipSuccess;
+    const int64_t grid64 = (int64_t)a.npad_blocks + a.T;
+    if (grid64 == 0) return hipSuccess;
+    if (grid64 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int grid = (int)grid64;
     switch (kind) {
         case kDispatchBf16:
             hipLaunchKernelGGL(k_dispatch<kDispatchBf16>, dim3(grid), dim3(threads), 0, stream, a);
