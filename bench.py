@@ -119,17 +119,18 @@ def calib_copy(dev) -> None:
     del a, b
 
 
-def load_traffic(kernel: str, khash: str):
+def load_traffic(kernel: str, khash: str, workload: str, path: str = None):
     """HBM bytes per launch of `kernel` (name with template arguments, e.g.
     k_dispatch<2>) from committed rocprofv3 counter runs, if they were taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    on the current kernel sources and on the same workload (the bytes of a
+    launch depend on its shape), else None."""
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     ent = t.get(kernel)
-    if not ent or ent.get("kernel_hash") != khash:
+    if not ent or ent.get("kernel_hash") != khash or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
 
@@ -335,7 +336,7 @@ def main():
     dom_ms = dom_live_ms if dom_live_ms is not None else k_ms[dominant]
     dom_gbps = nbytes[dominant] / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(kname[dominant], khash),
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(kname[dominant], khash, wl.name),
                 "kernel": kname[dominant], "call": dominant,
                 "algorithmic_bytes_per_launch": nbytes[dominant],
                 "avg_launch_us": round(dom_ms * 1e3, 2),
@@ -562,7 +563,8 @@ def bench_call(args):
         "config": {"workload": wl.name + "_" + args.step, "call": what, "tokens": T, "hidden": H,
                    "experts": wl.E, "topk": k, "expert_alignment": wl.A, "routing": wl.routing},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(kname, khash),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(kname, khash, wl.name + "_" + args.step),
                      "kernel": kname, "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(launch_ms * 1e3, 2), "timed": "events in the timed region"},
         "cpu_baseline": cpu,
@@ -668,7 +670,7 @@ def bench_gemm(args):
         "config": {"workload": wl.name + "_gemm", "tokens": wl.T, "hidden": H, "experts": wl.E, "topk": wl.k,
                    "n": N, "pairs": pairs, "rows_computed": rows, "expert_alignment": wl.A},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 5000.0, "unit": "TFLOP/s",
-                     "frac": round(achieved / 5000.0, 4), "traffic": load_traffic(kname, khash),
+                     "frac": round(achieved / 5000.0, 4), "traffic": load_traffic(kname, khash, wl.name + "_gemm"),
                      "kernel": kname,
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(launch_ms * 1e3, 1),
                      "timed": "events in the timed region"},

@@ -107,3 +107,16 @@ def test_kernel_hash_tracks_step_sources():
     for step, files in bench.KERNEL_SOURCES.items():
         for f in files:
             assert os.path.exists(os.path.join(bench.ROOT, "combine_ep_layout_10_amd", "csrc", f)), (step, f)
+
+
+def test_traffic_only_for_the_measured_workload_and_sources(tmp_path):
+    """Counter bytes are reported only for the workload and kernel sources
+    they were taken on: a launch's bytes depend on its shape."""
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps({"k_combine<true>": {"bytes_per_launch": 123, "kernel_hash": "abc",
+                                                 "workload": "v3"}}))
+    assert bench.load_traffic("k_combine<true>", "abc", "v3", str(p)) == 123
+    assert bench.load_traffic("k_combine<true>", "abc", "decode", str(p)) is None
+    assert bench.load_traffic("k_combine<true>", "abd", "v3", str(p)) is None
+    assert bench.load_traffic("k_combine<false>", "abc", "v3", str(p)) is None
+    assert bench.load_traffic("k_combine<true>", "abc", "v3", str(tmp_path / "missing.json")) is None
