@@ -109,9 +109,12 @@ __device__ __forceinline__ float block_amax16(const float f[16]) {
 // binary32 quotient; an all-zero block gives scale 0 and zero codes.
 //
 // scale = fl(amax / 448) by div448_bf16. The quotient is taken as
-// q = y + (x - y*scale) * r with r = 1/scale and y = x*r (one division per
-// lane instead of 16; the residual is exact by FMA), with x's sign copied
-// back so that -0 stays -0. Checked exhaustively on MI355X: for every pair of
+// q = y - (y*scale - x) * r with r = 1/scale and y = x*r (one division per
+// lane instead of 16; the residual y*scale - x is exact by FMA). No
+// copysign is needed for -0: for x != 0 the FMA's exact value
+// y - (y*scale - x)*r has x's sign, and rounding keeps it (a quotient that
+// underflows is a zero of x's sign); for x = +-0 the residual is +0 and
+// q = -(+0)*r + y = y, a zero of x's sign. Checked exhaustively on MI355X: for every pair of
 // finite bf16 values |x| <= amax with scale >= 2^-80, q equals the IEEE
 // quotient wherever |x / scale| >= 2^-10 (below that every code is a signed
 // zero and both agree). Smaller scales (amax < 2^-71) take the IEEE
@@ -127,8 +130,8 @@ __device__ __forceinline__ uint4 quantize16_amax(const float f[16], float amax, 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float y = f[i] * r;
-            const float e = __builtin_fmaf(-y, scale, f[i]);
-            q[i] = __builtin_copysignf(__builtin_fmaf(e, r, y), f[i]);
+            const float e = __builtin_fmaf(y, scale, -f[i]);
+            q[i] = __builtin_fmaf(-e, r, y);
         }
     } else {
 #pragma unroll
@@ -193,13 +196,12 @@ __device__ __forceinline__ void dispatch_store(const DispatchArgs& a, const Disp
             const int s = __builtin_amdgcn_readlane(my_s, j);
             if (s < 0) continue;
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+            // bf16(w * x) lands in the high half of a binary32 whose low
+            // half is bf16(0) = 0: the rounded product as a binary32, one
+            // conversion per value and no unpacking.
             float g[16];
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const uint32_t p = pack_bf16x2(wj * f[i], wj * f[i + 1]);
-                g[i] = bf16_to_f32(p & 0xFFFFu);
-                g[i + 1] = __uint_as_float(p & 0xFFFF0000u);
-            }
+            for (int i = 0; i < 16; ++i) g[i] = __uint_as_float(pack_bf16x2(0.0f, wj * f[i]));
             const float ag = bf16_to_f32(pack_bf16x2(fabsf(wj) * ax, 0.0f) & 0xFFFFu);
             float scale;
             const uint4 o = quantize16_amax(g, ag, scale);
