@@ -27,6 +27,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr int kMaxHidden = 1 << 24;
+
 // Byte offsets of every region of a workspace (256-byte aligned regions).
 struct WsMap {
     size_t flags, cnt, pad, eoff, doff, dtok, slot, rsrc, rw, bpart, dpart, fpart, total;
@@ -52,6 +54,9 @@ ep_status check_config(const ep_config* c) {
         return fail(EP_ERR_INVALID_ARG, "max_tokens %d out of range", c->max_tokens);
     if (c->hidden < 8 || c->hidden % 8 != 0)
         return fail(EP_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 8", c->hidden);
+    // Row stores go through buffer resources whose size and offsets are
+    // 32-bit byte counts: a bf16 row (2 * hidden bytes) must stay far below 2^32.
+    if (c->hidden > kMaxHidden) return fail(EP_ERR_INVALID_ARG, "hidden %d exceeds %d", c->hidden, kMaxHidden);
     if (c->idx_bits != 32 && c->idx_bits != 64)
         return fail(EP_ERR_INVALID_ARG, "idx_bits %d must be 32 or 64", c->idx_bits);
     if (c->mode == EP_MODE_COMPACT && c->expert_alignment < 1)

@@ -94,7 +94,7 @@ typedef enum { EP_BF16 = 0, EP_FP8_QUANTIZE = 1, EP_FP8_PREQUANT = 2 } ep_dtype;
  * (num_max_tokens_per_rank, hidden, num_topk, expert_alignment).
  * Limits: 1 <= num_experts <= 1024, 1 <= num_topk <= 32,
  * num_experts % num_dests == 0, max_tokens * num_topk < 2^31,
- * hidden >= 8 and hidden % 8 == 0 (hidden % 128 == 0 for FP8),
+ * 8 <= hidden <= 2^24 and hidden % 8 == 0 (hidden % 128 == 0 for FP8),
  * expert_alignment >= 1 (must be 1 in FIXED mode), capacity >= 1 in FIXED
  * mode, idx_bits 64 (int64 topk_idx, torch.topk's type) or 32. */
 typedef struct {

@@ -50,7 +50,7 @@ def test_rows_bound_and_workspace(name):
 
 @pytest.mark.parametrize("bad", [
     dict(num_experts=0), dict(num_experts=1025), dict(num_topk=0), dict(num_topk=33),
-    dict(num_dests=3), dict(hidden=100), dict(hidden=0), dict(idx_bits=16),
+    dict(num_dests=3), dict(hidden=100), dict(hidden=0), dict(hidden=(1 << 24) + 8), dict(idx_bits=16),
     dict(expert_alignment=0), dict(mode=2), dict(mode=F.EP_MODE_FIXED, capacity=0),
     dict(mode=F.EP_MODE_FIXED, capacity=4, expert_alignment=2), dict(flags=8), dict(max_tokens=-1),
     dict(max_tokens=1 << 30, num_topk=4),
