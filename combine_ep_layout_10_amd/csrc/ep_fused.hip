@@ -23,6 +23,94 @@
 
 namespace ep {
 
+// FIXED capacity (the decode layout), block 0's share: pairs per expert,
+// distinct tokens per destination and the error bits, from the ids every
+// block has loaded (this wave's IT groups of 64 pairs starting at `base`);
+// writes cnt, pad = min(cnt, C), expert_off = e*C, dest_off, dest_tokens and
+// the error word. Every thread of the block must call it.
+template <int IT>
+__device__ __forceinline__ void fixed_publish_counts(const LayoutArgs& a, const int ids[IT], const bool val[IT],
+                                                     bool bad, int64_t base, int32_t* lds) {
+    const int tid = threadIdx.x;
+    int32_t* hist = lds;        // [E]
+    int32_t* dh = lds + a.E;    // [D]
+    for (int i = tid; i < a.E + a.D; i += blockDim.x) lds[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        if (val[it]) atomicAdd(&hist[ids[it]], 1);
+        const int dd = val[it] ? ids[it] / a.epd : -1;
+        if (first_in_dest(a, base + it * kWave, dd, val[it])) atomicAdd(&dh[dd], 1);
+    }
+    const bool any_bad = __syncthreads_or(bad);
+    bool over = false;
+    for (int e = tid; e < a.E; e += blockDim.x) {
+        const int n = hist[e];
+        a.cnt[e] = n;
+        a.pad[e] = n < a.C ? n : a.C;
+        over |= n > a.C;
+    }
+    for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = e * a.C;
+    for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = d * a.epd * a.C;
+    for (int d = tid; d < a.D; d += blockDim.x) a.dest_tokens[d] = dh[d];
+    const bool any_over = __syncthreads_or(over);
+    if (tid == 0) a.err_flags[0] = (any_bad ? EP_ERRFLAG_BAD_ID : 0u) | (any_over ? EP_ERRFLAG_OVERFLOW : 0u);
+}
+
+// FIXED capacity: the rows of token t's k pairs. Pair p = t*k + j of expert
+// e goes to row e*C + r, r = the number of valid pairs p' < p with expert e
+// (the stable order), or nowhere when r >= C; so a token block needs only
+// these k counts, not the whole layout. Each wave counts, for every j, the
+// matching pairs among its loaded ids with one ballot per group of 64; the
+// per-wave counts are summed in wave order. Part 0 of the token also writes
+// the pairs' slot, row_src and row_w. The k rows land in s_slot. Every
+// thread of the block must call it (`tok` is block-uniform).
+template <int IT>
+__device__ __forceinline__ void fixed_token_slots(const LayoutArgs& a, const int ids[IT], const bool val[IT],
+                                                  int64_t base, bool tok, int t, int part, int32_t* s_slot) {
+    __shared__ int32_t s_e[kMaxTopk];
+    __shared__ int32_t s_wc[kLayoutWaves][kMaxTopk];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t p0 = (int64_t)t * a.k;
+    if (tok) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int64_t p = base + it * kWave + lane;
+            if (p >= p0 && p < p0 + a.k) s_e[p - p0] = val[it] ? ids[it] : -1;
+        }
+    }
+    __syncthreads();
+    if (tok) {
+        for (int j = 0; j < a.k; ++j) {
+            const int e = s_e[j];  // the same in every lane: a uniform branch
+            int n = 0;
+            if (e >= 0) {
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const int64_t p = base + it * kWave + lane;
+                    n += __popcll(ballot64(val[it] && ids[it] == e && p < p0 + j));
+                }
+            }
+            if (lane == 0) s_wc[w][j] = n;
+        }
+    }
+    __syncthreads();
+    if (tok && tid < a.k) {
+        const int e = s_e[tid];
+        int r = 0;
+        for (int ww = 0; ww < kLayoutWaves; ++ww) r += s_wc[ww][tid];
+        const int32_t s = (e >= 0 && r < a.C) ? e * a.C + r : -1;
+        s_slot[tid] = s;
+        if (part == 0) {
+            a.slot[p0 + tid] = s;
+            if (s >= 0) {
+                a.row_src[s] = (int32_t)(p0 + tid);
+                if (a.w) a.row_w[s] = a.w[p0 + tid];
+            }
+        }
+    }
+}
+
 template <int IT, int KIND>
 __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, DispatchArgs da) {
     extern __shared__ int32_t lds[];
@@ -35,6 +123,31 @@ __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, D
     const int c_end = min((part + 1) * da.seg, dispatch_nvec<KIND>(da));
     const bool act = tok && (int)threadIdx.x < da.seg && c < c_end;
     const DispatchRaw raw = dispatch_load<KIND>(da, t, c, act);
+
+    if (la.mode == EP_MODE_FIXED) {  // uniform across the grid
+        const int lane = threadIdx.x & 63;
+        const int64_t P = (int64_t)la.T * la.k;
+        const int64_t base = (int64_t)(threadIdx.x >> 6) * (IT * kWave);
+        int ids[IT];
+        bool val[IT];
+        bool bad = false;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int64_t p = base + it * kWave + lane;
+            bool v = false, b = false;
+            ids[it] = p < P ? load_id(la, p, v, b) : 0;
+            val[it] = v;
+            bad |= b;
+        }
+        fixed_token_slots<IT>(la, ids, val, base, tok, t, part, s_slot);
+        if (blockIdx.x == 0) fixed_publish_counts<IT>(la, ids, val, bad, base, lds);
+        __syncthreads();
+        if (!tok || (int)threadIdx.x >= ((da.seg + 63) & ~63)) return;
+        const int my_s = lane < la.k ? s_slot[lane] : -1;
+        const DispatchVec d = dispatch_encode<KIND>(raw);
+        dispatch_store<KIND>(da, d, c, act, my_s, 0.0f);
+        return;
+    }
 
     SmallLayout<IT> L;
     const bool lead = blockIdx.x == 0;

@@ -103,13 +103,16 @@ def test_random_layouts(T, E, k, A, D):
     _run_small(T, 64, E, k, A=A, D=D, seed=T + E)
 
 
-def _layout_every_table(mode, T, E, k, A, D, C, tables):
+def _layout_every_table(mode, T, E, k, A, D, C, tables, forward=False):
     """One ep_layout launch per routing table, each into its own slice of one
     workspace, one synchronisation, then every table's layout against the
     oracle (which equals the O(P^2) brute-force definition on these same
-    tables: tests/test_oracle_layout.py)."""
+    tables: tests/test_oracle_layout.py). forward=True builds each layout with
+    ep_dispatch_forward (BF16) instead and also checks every table's receive
+    rows: the token's row where the layout puts a pair, untouched elsewhere."""
     n = len(tables)
-    log("every table: mode=%d T=%d E=%d k=%d A=%d D=%d C=%d, %d tables" % (mode, T, E, k, A, D, C, n))
+    log("every table: mode=%d T=%d E=%d k=%d A=%d D=%d C=%d forward=%d, %d tables"
+        % (mode, T, E, k, A, D, C, forward, n))
     cfg = ops.Config(max_tokens=T, hidden=128, num_experts=E, num_topk=k, num_dests=D,
                      expert_alignment=A, capacity=C, mode=mode)
     ws = -(-cfg.workspace_bytes() // 256) * 256
@@ -117,8 +120,17 @@ def _layout_every_table(mode, T, E, k, A, D, C, tables):
     idx_all = to_dev(np.ascontiguousarray(np.asarray(tables, np.int64)))
     w = ((np.arange(T * k, dtype=np.float32) + 1) / 8).reshape(T, k)
     w_dev = to_dev(w)
-    handles = [ops.layout(cfg, idx_all[i], w_dev, workspace=big[i * ws:(i + 1) * ws]) for i in range(n)]
+    Rb = cfg.recv_rows_bound()
+    if forward:
+        x = f32_to_bf16_bits(np.random.default_rng(T * 100 + C).standard_normal((T, 128)).astype(np.float32))
+        x_dev = to_dev_bf16(x)
+        recv_all = torch.full((n, Rb, 128), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        handles = [ops.dispatch_forward(cfg, idx_all[i], x_dev, ops.BF16, topk_w=w_dev,
+                                        workspace=big[i * ws:(i + 1) * ws], recv=recv_all[i])[0] for i in range(n)]
+    else:
+        handles = [ops.layout(cfg, idx_all[i], w_dev, workspace=big[i * ws:(i + 1) * ws]) for i in range(n)]
     torch.cuda.synchronize()
+    recv_host = bf16_host(recv_all) if forward else None
     whole = big.cpu().numpy()
     base = big.data_ptr()
 
@@ -126,7 +138,6 @@ def _layout_every_table(mode, T, E, k, A, D, C, tables):
         off = ptr - base
         return whole[off: off + count * np.dtype(dt).itemsize].view(dt)
 
-    Rb = cfg.recv_rows_bound()
     for i, (h, tab) in enumerate(zip(handles, tables)):
         lay = oracle.layout(mode, T, E, k, A, D, C, np.asarray(tab, np.int64), w)
         c = h.c
@@ -140,6 +151,10 @@ def _layout_every_table(mode, T, E, k, A, D, C, tables):
         assert np.array_equal(field(c.row_src, Rb, np.int32)[rows], lay["row_src"][rows]), (i, tab)
         assert np.array_equal(field(c.row_w, Rb, np.float32)[rows].view(np.uint32),
                               lay["row_w"][rows].view(np.uint32)), (i, tab)
+        if forward:
+            ref = oracle.dispatch_bf16(lay, x, k)
+            assert np.array_equal(recv_host[i][rows], ref[rows]), (i, tab)
+            assert np.all(recv_host[i][np.setdiff1d(np.arange(Rb), rows)] == 0xFFFF), (i, tab)
 
 
 def test_every_tiny_routing_table():
@@ -157,6 +172,17 @@ def test_every_tiny_fixed_table():
     rows = list(itertools.product(range(3), repeat=2))
     for C in (1, 2):
         _layout_every_table(oracle.MODE_FIXED, 3, 3, 2, 1, 1, C, list(itertools.product(rows, repeat=3)))
+
+
+def test_every_tiny_fixed_table_single_launch():
+    """The same tables through ep_dispatch_forward, whose single launch
+    builds FIXED layouts from per-token rank counts (no block builds the
+    whole layout): handle arrays, flags and receive rows."""
+    import itertools
+    rows = list(itertools.product(range(3), repeat=2))
+    for C in (1, 2):
+        _layout_every_table(oracle.MODE_FIXED, 3, 3, 2, 1, 1, C, list(itertools.product(rows, repeat=3)),
+                            forward=True)
 
 
 @pytest.mark.parametrize("T,H,E,k,A,D,dispatch", [
@@ -241,6 +267,9 @@ def test_argument_errors_enqueue_nothing():
     (128, 256, 8, 1, 1, 128, 1, "fp8", 0.0, 0.0),        # decode shape (FIXED), single launch
     (100, 64, 8, 16, 4, 0, 0, "fp8", 0.0, 0.0),          # padding rows cleared by the same launch
     (128, 64, 8, 1, 1, 12, 1, "bf16", 0.0, 0.0),         # FIXED overflow
+    (200, 64, 6, 1, 4, 20, 1, "fp8", 0.1, 0.02),         # FIXED, P = 1200 (four groups per wave), D = 4, masked/bad ids
+    (512, 512, 8, 1, 8, 16, 1, "bf16", 0.1, 0.02),       # FIXED, P = 4096, E = 512, overflow, repeated experts
+    (1, 4, 3, 1, 2, 1, 1, "bf16", 0.0, 0.0),             # FIXED, one token
     (129, 64, 8, 32, 2, 0, 0, "bf16", 0.0, 0.0),         # P = 1032: four groups per wave
     (512, 512, 8, 8, 8, 0, 0, "fp8", 0.1, 0.02),         # P = 4096, E = 512: largest single launch
     (513, 512, 8, 8, 8, 0, 0, "bf16", 0.0, 0.0),         # P = 4104: layout + dispatch launches
