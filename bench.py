@@ -138,7 +138,7 @@ def load_traffic(kernel: str, khash: str, workload: str, path: str = None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library computes one GPU's share and has no multi-GPU path "
               "(--gpus %d requested). Run with --gpus 1." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
