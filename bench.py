@@ -446,6 +446,10 @@ def main():
     kernels.update({"bytes": nbytes, "kernel_bytes": {kname[n]: nbytes[n] for n in names}, "kernel_hash": khash,
                     "cold_cache": flushed, "copy_1GiB_GBps": copy_ceiling,
                     "fill_1GiB_GBps": fill_ceiling})
+    # the dominant kernel against the rates measured in this run (a device
+    # copy: half reads, half writes; a fill: writes only)
+    for key, ceil in (("copy", copy_ceiling), ("fill", fill_ceiling)):
+        kernels["dominant_frac_of_" + key] = round(dom_gbps / ceil, 4) if ceil else None
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,

@@ -126,7 +126,13 @@ __device__ __forceinline__ uint4 quantize16_amax(const float f[16], float amax, 
     const float scale = div448_bf16(amax);
     float q[16];
     if (scale >= 0x1p-80f) {
-        const float r = 1.0f / scale;
+        // 1/scale from the hardware reciprocal and one Newton step: checked on
+        // MI355X against the IEEE quotient 1/scale for every scale this branch
+        // can see (fl(a/448) for each of the 25,504 positive finite bfloat16 a
+        // with a scale >= 2^-80): identical, so r is the correctly rounded
+        // reciprocal.
+        const float r0 = __builtin_amdgcn_rcpf(scale);
+        const float r = __builtin_fmaf(__builtin_fmaf(-scale, r0, 1.0f), r0, r0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float y = f[i] * r;
