@@ -669,7 +669,11 @@ def test_repeat_is_bit_identical():
 
 @pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3", "skewed_v3"])
 def test_workload_full_size(name):
-    """Every workload at its full size: layout, dispatch and combine."""
+    """Every workload at its full size: layout, dispatch and combine through
+    ep_layout + ep_dispatch, then the calls bench.py times for it (one
+    ep_dispatch_forward, the weighted combine and, for the aligned layouts,
+    the weighted BF16 combine_backward and dispatch_backward with the
+    weight-gradient gather), each against the oracle."""
     log("workload %s: preparing inputs and oracle" % name)
     case = workload_case(name)
     wl, inp, lay = case["wl"], case["inp"], case["lay"]
@@ -701,5 +705,48 @@ def test_workload_full_size(name):
     log("workload %s: combine max ulp %d, differing %d" % (name, d.max(), int((d > 0).sum())))
     assert d.max() <= 1
     assert np.array_equal(host(vals).view(np.uint32), case["out_vals"].view(np.uint32))
-    del y, out, x
+    del out, vals, h
+    torch.cuda.empty_cache()
+
+    log("workload %s: bench calls (dispatch_forward, combine, backward duals)" % name)
+    R = cfg.recv_rows_bound()
+    w = to_dev(inp["topk_w"])
+    if wl.dispatch == "fp8":
+        recv = torch.full((R, wl.H), 0xEE, dtype=torch.uint8, device="cuda")
+        rs = torch.full((R, wl.H // 128), -7.0, dtype=torch.float32, device="cuda")
+        h = ops.dispatch_forward(cfg, to_dev(inp["topk_idx"]), x, ops.FP8_QUANTIZE, topk_w=w, recv=recv,
+                                 recv_scales=rs)[0]
+        compare_layout(h, lay)
+        assert np.array_equal(host(recv)[rows], case["recv"][rows])
+        assert np.array_equal(host(rs)[rows].view(np.uint32), case["recv_scales"][rows].view(np.uint32))
+        untouched = np.setdiff1d(np.arange(R), rows)
+        assert np.all(host(recv)[untouched] == 0xEE)
+        del recv, rs
+    else:
+        recv = torch.full((R, wl.H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        h = ops.dispatch_forward(cfg, to_dev(inp["topk_idx"]), x, ops.BF16, topk_w=w, recv=recv)[0]
+        compare_layout(h, lay)
+        got_recv = bf16_host(recv)
+        assert np.array_equal(got_recv[rows], case["recv"][rows])
+        assert np.all(got_recv[np.setdiff1d(np.arange(R), rows)] == 0xFFFF)
+        del recv, got_recv
+    out = ops.combine(h, y, w)
+    assert bf16_ulp_distance(bf16_host(out), case["out"]).max() <= 1
+    del out
+    if wl.mode == oracle.MODE_COMPACT:
+        rng = np.random.default_rng(5)
+        go = f32_to_bf16_bits(rng.standard_normal((wl.T, wl.H)).astype(np.float32))
+        grw = rng.standard_normal(R).astype(np.float32)
+        ref = oracle.combine_backward_bf16(lay, go, wl.k, inp["topk_w"])
+        gy = ops.combine_backward(h, to_dev_bf16(go), ops.BF16, w)
+        prow = np.arange(lay["rows"])
+        assert np.array_equal(bf16_host(gy)[prow], ref[prow]), "combine_backward"
+        del gy, ref
+        # the expert-output rows serve as the receive-row gradients
+        ref_x, ref_w = oracle.dispatch_backward(lay, inp["y"], wl.k, grw)
+        gx, gw = ops.dispatch_backward(h, y, to_dev(grw))
+        assert np.array_equal(bf16_host(gx), ref_x), "dispatch_backward"
+        assert np.array_equal(host(gw).view(np.uint32), ref_w.view(np.uint32))
+        del gx, gw
+    del y, x, h
     torch.cuda.empty_cache()
