@@ -5,11 +5,14 @@
 //
 // The layout has a grid-wide dependency (a token's row depends on the
 // counts of every expert before it), so instead of waiting on other blocks
-// every block recomputes the whole layout of the batch in LDS (pairs <=
-// 4096, E <= 512: a few KiB of ids read from L2 per block). The first
-// blocks copy one piece (seg vectors) of one token's row each, taking the
-// token's slots from the lanes that ranked its pairs; the last ones
-// zero-fill padding rows; block 0 also writes the handle's arrays. A token
+// every block derives what it needs from all the ids of the batch (pairs <=
+// 4096, E <= 512: a few KiB read from L2 per block). In the aligned
+// (COMPACT) layout every block recomputes the whole layout in LDS; in FIXED
+// capacity a token block only counts the earlier pairs of its own pairs'
+// experts (its rows are e*C + that count). The first blocks copy one piece
+// (seg vectors) of one token's row each; the last ones zero-fill padding
+// rows; block 0 also writes the handle's arrays (in FIXED mode each token
+// writes its own pairs' slots and rows, block 0 the counts). A token
 // block issues the loads of its piece of x before the layout work, so both
 // round trips overlap. Small batches have few tokens, so rows are split over
 // several blocks to reach every CU, but the grid is kept to one block per CU:

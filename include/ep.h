@@ -178,8 +178,9 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
  * recv_scales) are bit-identical to ep_layout followed by ep_dispatch.
  * Small batches (num_tokens * k <= 4096 and E <= 512, the decode sizes of
  * README "Example use in inference decoding") take a single kernel launch:
- * every block recomputes the small layout in LDS, so no block waits on
- * another. Larger batches enqueue the layout kernels and then the dispatch
+ * every block derives its rows from all the batch's ids (the whole small
+ * layout in LDS, or in FIXED mode only the ranks of its own pairs), so no
+ * block waits on another. Larger batches enqueue the layout kernels and then the dispatch
  * kernel. Never synchronises. */
 ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
                               const float* topk_w, void* workspace, size_t workspace_bytes,
