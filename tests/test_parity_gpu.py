@@ -98,6 +98,7 @@ def test_tiny_hand_example():
     (16384, 256, 8, 128, 8),     # 128 count blocks x 256 experts: the largest matrix reduced inline
     (16400, 256, 8, 128, 8),     # 129 count blocks: one-block scan launch
     (40000, 256, 4, 16, 8),      # many count blocks, 3 kernels
+    (50, 4, 2, 1000, 2),         # alignment 1000: 250 zero-fill blocks per expert, most rows padding
 ])
 def test_random_layouts(T, E, k, A, D):
     _run_small(T, 64, E, k, A=A, D=D, seed=T + E)
