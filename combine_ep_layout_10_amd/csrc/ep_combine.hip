@@ -41,7 +41,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
             for (int u = 0; u < 8; ++u) {
                 s[u] = j0 + u < a.k ? __builtin_amdgcn_readlane(my_s, j0 + u) : -1;
                 v[u] = make_uint4(0u, 0u, 0u, 0u);
-                if (s[u] >= 0) v[u] = load_stream((const uint4*)(a.y + (int64_t)s[u] * a.H) + c);
+                if (s[u] >= 0) v[u] = load_row_stream(a.y + (int64_t)s[u] * a.H, 2u * (uint32_t)a.H, 16u * c);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(1024) void k_weight_grad(WeightGradArgs a) {
             for (int u = 0; u < 8; ++u) {
                 s[u] = j0 + u < a.k ? __builtin_amdgcn_readlane(my_s, j0 + u) : -1;
                 v[u] = make_uint4(0u, 0u, 0u, 0u);
-                if (s[u] >= 0) v[u] = load_stream((const uint4*)(a.y + (int64_t)s[u] * a.H) + c);
+                if (s[u] >= 0) v[u] = load_row_stream(a.y + (int64_t)s[u] * a.H, 2u * (uint32_t)a.H, 16u * c);
             }
             float g[8];
             g[0] = bf16_to_f32(gv.x & 0xFFFFu);

@@ -48,15 +48,7 @@ __device__ __forceinline__ float div448_bf16(float a) {
 
 // ---------------------------------------------------------------- memory
 
-// Streaming (non-temporal) 16-byte load for data read once (the combine's
-// gathered rows): on gfx950 it keeps single-use rows from displacing
-// reusable lines in L2 and MALL (measured: 214 -> 181 us for the V3 combine).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 load_stream(const void* p) {
-    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // Streaming 16-byte store into one row through a buffer resource, with the
 // cache policy sc0 sc1 nt (LLVM's GLC | SLC | SCC bits, read by gfx950 as
@@ -73,6 +65,24 @@ __device__ __forceinline__ void store_row_stream(void* row, uint32_t row_bytes, 
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)row_bytes, kBufferFlags);
     const u32x4_t x = {v.x, v.y, v.z, v.w};
     __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kCpolStream);
+}
+
+// Streaming (nt) 16-byte load from one row through a buffer resource, for
+// rows gathered once (the combine's expert-output rows): nt keeps single-use
+// rows from displacing reusable lines in L2 and MALL, and the row's base sits
+// in scalar registers, so a lane adds only its 32-bit offset. Measured on
+// MI355X in the 8192 x 7168 x top-8 combine: 178.2-178.8 us against
+// 180.2-181.4 us for non-temporal global loads with 64-bit per-lane
+// addresses, three runs in alternation (sc0 nt, sc1 nt and sc0 sc1 nt the
+// same within noise; without nt 191-193 us). `row` must be the same in every
+// lane; loads at or past `row_bytes` return zeros.
+constexpr int kCpolLoadStream = 2;
+
+__device__ __forceinline__ uint4 load_row_stream(const void* row, uint32_t row_bytes, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)row_bytes, kBufferFlags);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolLoadStream);
+    return make_uint4(x.x, x.y, x.z, x.w);
 }
 
 // ---------------------------------------------------------------- wave ops
