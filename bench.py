@@ -593,7 +593,7 @@ def bench_gemm(args):
         sys.exit(1)
     wl = WORKLOADS[args.workload]
     if wl.dispatch != "fp8":
-        print("--step gemm needs an FP8 workload (v3, skewed_v3, decode)", file=sys.stderr)
+        print("--step gemm needs an FP8 workload (v3, skewed_v3, skewed_v3_s06, decode)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     N, H = args.gemm_n, wl.H

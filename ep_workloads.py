@@ -2,7 +2,7 @@
 
 This module is the only code shared by the CPU oracle side and the GPU side:
 it draws the inputs (hidden states, routing, weights, expert outputs) and
-holds the five workload shapes. It contains none of the dispatch/combine
+holds the workload shapes. It contains none of the dispatch/combine
 arithmetic: no layout, no copies, no quantisation, no reduction.
 
 Shapes follow the DeepEP README (community translation), section
@@ -80,6 +80,11 @@ WORKLOADS = {
                           zipf_s=1.2, outlier_frac=0.01),
     "decode": Workload("decode", T=128, H=7168, E=256, k=8, A=1, D=1,
                        mode=MODE_FIXED, C=128, dispatch="fp8", routing="uniform"),
+    # the skewed shape at the stated load of the hottest expert (about 10x
+    # the mean: 10.8x at seed 0), which Zipf s = 1.2 overshoots (29.7x)
+    "skewed_v3_s06": Workload("skewed_v3_s06", T=8192, H=7168, E=256, k=8, A=128, D=8,
+                              mode=MODE_COMPACT, C=0, dispatch="fp8", routing="zipf",
+                              zipf_s=0.6, outlier_frac=0.01),
 }
 
 

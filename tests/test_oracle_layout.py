@@ -127,7 +127,7 @@ def test_random_small_with_masks_and_bad_ids(seed):
         assert lay["flags"] == lay32["flags"]
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "v3", "skewed_v3", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "v3", "skewed_v3", "skewed_v3_s06", "decode"])
 def test_workload_invariants(name):
     """P1-P3 at the workloads' real shapes: counts are numpy's bincount,
     slots equal the stable argsort of the expert ids mapped through the

@@ -668,7 +668,7 @@ def test_repeat_is_bit_identical():
 
 # ---------------------------------------------------------------- full workloads
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3", "skewed_v3"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3", "skewed_v3", "skewed_v3_s06"])
 def test_workload_full_size(name):
     """Every workload at its full size: layout, dispatch and combine through
     ep_layout + ep_dispatch, then the calls bench.py times for it (one
