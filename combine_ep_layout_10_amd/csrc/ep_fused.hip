@@ -26,17 +26,23 @@
 
 namespace ep {
 
-// FIXED capacity (the decode layout), block 0's share: pairs per expert,
+// Layouts whose rows follow from counts alone (FIXED capacity, and the
+// aligned layout with alignment 1), block 0's share: pairs per expert,
 // distinct tokens per destination and the error bits, from the ids every
 // block has loaded (this wave's IT groups of 64 pairs starting at `base`);
-// writes cnt, pad = min(cnt, C), expert_off = e*C, dest_off, dest_tokens and
-// the error word. Every thread of the block must call it.
+// writes cnt, pad, expert_off, dest_off, dest_tokens and the error word.
+// FIXED: pad = min(cnt, C), expert_off = e*C. Alignment 1: pad = cnt,
+// expert_off = the exclusive scan of cnt. Every thread of the block must
+// call it.
 template <int IT>
-__device__ __forceinline__ void fixed_publish_counts(const LayoutArgs& a, const int ids[IT], const bool val[IT],
-                                                     bool bad, int64_t base, int32_t* lds) {
+__device__ __forceinline__ void rank_layout_publish_counts(const LayoutArgs& a, const int ids[IT], const bool val[IT],
+                                                           bool bad, int64_t base, int32_t* lds) {
+    __shared__ int tmp[17];
     const int tid = threadIdx.x;
-    int32_t* hist = lds;        // [E]
-    int32_t* dh = lds + a.E;    // [D]
+    const bool fixed = a.mode == EP_MODE_FIXED;
+    int32_t* hist = lds;                 // [E]
+    int32_t* dh = lds + a.E;             // [D]
+    int32_t* off = lds + a.E + a.D;      // [E+1]
     for (int i = tid; i < a.E + a.D; i += blockDim.x) lds[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -50,30 +56,43 @@ __device__ __forceinline__ void fixed_publish_counts(const LayoutArgs& a, const 
     for (int e = tid; e < a.E; e += blockDim.x) {
         const int n = hist[e];
         a.cnt[e] = n;
-        a.pad[e] = n < a.C ? n : a.C;
-        over |= n > a.C;
+        a.pad[e] = fixed ? (n < a.C ? n : a.C) : n;
+        over |= fixed && n > a.C;
     }
-    for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = e * a.C;
-    for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = d * a.epd * a.C;
+    if (fixed) {
+        for (int e = tid; e <= a.E; e += blockDim.x) off[e] = e * a.C;
+    } else {  // E <= 512 < blockDim: one expert per thread
+        int total;
+        const int excl = block_exclusive_scan(tid < a.E ? hist[tid] : 0, tmp, &total);
+        if (tid < a.E) off[tid] = excl;
+        if (tid == 0) off[a.E] = total;
+    }
+    __syncthreads();
+    for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = off[e];
+    for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = off[d * a.epd];
     for (int d = tid; d < a.D; d += blockDim.x) a.dest_tokens[d] = dh[d];
     const bool any_over = __syncthreads_or(over);
     if (tid == 0) a.err_flags[0] = (any_bad ? EP_ERRFLAG_BAD_ID : 0u) | (any_over ? EP_ERRFLAG_OVERFLOW : 0u);
 }
 
-// FIXED capacity: the rows of token t's k pairs. Pair p = t*k + j of expert
-// e goes to row e*C + r, r = the number of valid pairs p' < p with expert e
-// (the stable order), or nowhere when r >= C; so a token block needs only
-// these k counts, not the whole layout. Each wave counts, for every j, the
-// matching pairs among its loaded ids with one ballot per group of 64; the
-// per-wave counts are summed in wave order. Part 0 of the token also writes
-// the pairs' slot, row_src and row_w. The k rows land in s_slot. Every
-// thread of the block must call it (`tok` is block-uniform).
+// The rows of token t's k pairs in a layout whose rows follow from counts.
+// Pair p = t*k + j of expert e has rank r = the number of valid pairs
+// p' < p with expert e (the stable order). FIXED: row e*C + r, or nowhere
+// when r >= C. Alignment 1: row b + r, b = the number of valid pairs with an
+// expert below e (the exclusive scan of the counts at e). So a token block
+// needs only these 2k counts, not the whole layout. Each wave counts, for
+// every j, the matching pairs among its loaded ids with one ballot per group
+// of 64 and count; the per-wave counts are summed in wave order. Part 0 of
+// the token also writes the pairs' slot, row_src and row_w. The k rows land
+// in s_slot. Every thread of the block must call it (`tok` is block-uniform).
 template <int IT>
-__device__ __forceinline__ void fixed_token_slots(const LayoutArgs& a, const int ids[IT], const bool val[IT],
-                                                  int64_t base, bool tok, int t, int part, int32_t* s_slot) {
+__device__ __forceinline__ void rank_layout_token_slots(const LayoutArgs& a, const int ids[IT], const bool val[IT],
+                                                        int64_t base, bool tok, int t, int part, int32_t* s_slot) {
     __shared__ int32_t s_e[kMaxTopk];
     __shared__ int32_t s_wc[kLayoutWaves][kMaxTopk];
+    __shared__ int32_t s_wb[kLayoutWaves][kMaxTopk];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool fixed = a.mode == EP_MODE_FIXED;
     const int64_t p0 = (int64_t)t * a.k;
     if (tok) {
 #pragma unroll
@@ -86,23 +105,30 @@ __device__ __forceinline__ void fixed_token_slots(const LayoutArgs& a, const int
     if (tok) {
         for (int j = 0; j < a.k; ++j) {
             const int e = s_e[j];  // the same in every lane: a uniform branch
-            int n = 0;
+            int n = 0, nb = 0;
             if (e >= 0) {
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
                     const int64_t p = base + it * kWave + lane;
                     n += __popcll(ballot64(val[it] && ids[it] == e && p < p0 + j));
+                    if (!fixed) nb += __popcll(ballot64(val[it] && ids[it] < e));
                 }
             }
-            if (lane == 0) s_wc[w][j] = n;
+            if (lane == 0) {
+                s_wc[w][j] = n;
+                if (!fixed) s_wb[w][j] = nb;
+            }
         }
     }
     __syncthreads();
     if (tok && tid < a.k) {
         const int e = s_e[tid];
-        int r = 0;
+        int r = 0, b = 0;
         for (int ww = 0; ww < kLayoutWaves; ++ww) r += s_wc[ww][tid];
-        const int32_t s = (e >= 0 && r < a.C) ? e * a.C + r : -1;
+        if (!fixed)
+            for (int ww = 0; ww < kLayoutWaves; ++ww) b += s_wb[ww][tid];
+        int32_t s = -1;
+        if (e >= 0) s = fixed ? (r < a.C ? e * a.C + r : -1) : b + r;
         s_slot[tid] = s;
         if (part == 0) {
             a.slot[p0 + tid] = s;
@@ -127,7 +153,7 @@ __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, D
     const bool act = tok && (int)threadIdx.x < da.seg && c < c_end;
     const DispatchRaw raw = dispatch_load<KIND>(da, t, c, act);
 
-    if (la.mode == EP_MODE_FIXED) {  // uniform across the grid
+    if (la.mode == EP_MODE_FIXED || la.A == 1) {  // rows follow from counts; uniform across the grid
         const int lane = threadIdx.x & 63;
         const int64_t P = (int64_t)la.T * la.k;
         const int64_t base = (int64_t)(threadIdx.x >> 6) * (IT * kWave);
@@ -142,8 +168,8 @@ __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, D
             val[it] = v;
             bad |= b;
         }
-        fixed_token_slots<IT>(la, ids, val, base, tok, t, part, s_slot);
-        if (blockIdx.x == 0) fixed_publish_counts<IT>(la, ids, val, bad, base, lds);
+        rank_layout_token_slots<IT>(la, ids, val, base, tok, t, part, s_slot);
+        if (blockIdx.x == 0) rank_layout_publish_counts<IT>(la, ids, val, bad, base, lds);
         __syncthreads();
         if (!tok || (int)threadIdx.x >= ((da.seg + 63) & ~63)) return;
         const int my_s = lane < la.k ? s_slot[lane] : -1;

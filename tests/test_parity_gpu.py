@@ -166,6 +166,22 @@ def test_every_tiny_routing_table():
     _layout_every_table(oracle.MODE_COMPACT, 4, 4, 2, 2, 2, 0, list(itertools.product(rows, repeat=4)))
 
 
+def test_every_tiny_routing_table_single_launch():
+    """Every 4-token, 4-expert top-2 distinct table (20,736), alignment 1,
+    two destinations, through ep_dispatch_forward: its single launch builds
+    alignment-1 layouts from per-token counts (rows = pairs with a smaller
+    expert id + earlier pairs of the same expert); handle arrays, flags and
+    receive rows. Then every 3-token, 3-expert top-2 table with repeated
+    experts (9^3)."""
+    import itertools
+    rows = list(itertools.permutations(range(4), 2))
+    _layout_every_table(oracle.MODE_COMPACT, 4, 4, 2, 1, 2, 0, list(itertools.product(rows, repeat=4)),
+                        forward=True)
+    rows = list(itertools.product(range(3), repeat=2))
+    _layout_every_table(oracle.MODE_COMPACT, 3, 3, 2, 1, 1, 0, list(itertools.product(rows, repeat=3)),
+                        forward=True)
+
+
 def test_every_tiny_fixed_table():
     """FIXED capacity 1 and 2: every table of 3 tokens, 3 experts, top-2 with
     repeats allowed (9^3 tables), overflow flags included."""
@@ -265,6 +281,8 @@ def test_argument_errors_enqueue_nothing():
 
 @pytest.mark.parametrize("T,E,k,A,D,C,mode,dispatch,masked,bad", [
     (128, 16, 2, 1, 1, 0, 0, "bf16", 0.0, 0.0),          # tiny shape, single launch
+    (300, 40, 4, 1, 4, 0, 0, "bf16", 0.1, 0.02),         # alignment 1, P = 1200 (four groups per wave), masked/bad ids
+    (512, 512, 8, 1, 8, 0, 0, "fp8", 0.05, 0.01),        # alignment 1, P = 4096, E = 512, repeated experts
     (128, 256, 8, 1, 1, 128, 1, "fp8", 0.0, 0.0),        # decode shape (FIXED), single launch
     (100, 64, 8, 16, 4, 0, 0, "fp8", 0.0, 0.0),          # padding rows cleared by the same launch
     (128, 64, 8, 1, 1, 12, 1, "bf16", 0.0, 0.0),         # FIXED overflow
