@@ -60,16 +60,17 @@ __device__ __forceinline__ void rank_layout_publish_counts(const LayoutArgs& a, 
         over |= fixed && n > a.C;
     }
     if (fixed) {
-        for (int e = tid; e <= a.E; e += blockDim.x) off[e] = e * a.C;
+        for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = e * a.C;
+        for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = d * a.epd * a.C;
     } else {  // E <= 512 < blockDim: one expert per thread
         int total;
         const int excl = block_exclusive_scan(tid < a.E ? hist[tid] : 0, tmp, &total);
         if (tid < a.E) off[tid] = excl;
         if (tid == 0) off[a.E] = total;
+        __syncthreads();
+        for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = off[e];
+        for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = off[d * a.epd];
     }
-    __syncthreads();
-    for (int e = tid; e <= a.E; e += blockDim.x) a.expert_off[e] = off[e];
-    for (int d = tid; d <= a.D; d += blockDim.x) a.dest_off[d] = off[d * a.epd];
     for (int d = tid; d < a.D; d += blockDim.x) a.dest_tokens[d] = dh[d];
     const bool any_over = __syncthreads_or(over);
     if (tid == 0) a.err_flags[0] = (any_bad ? EP_ERRFLAG_BAD_ID : 0u) | (any_over ? EP_ERRFLAG_OVERFLOW : 0u);
