@@ -6,13 +6,15 @@
 // The layout has a grid-wide dependency (a token's row depends on the
 // counts of every expert before it), so instead of waiting on other blocks
 // every block derives what it needs from all the ids of the batch (pairs <=
-// 4096, E <= 512: a few KiB read from L2 per block). In the aligned
-// (COMPACT) layout every block recomputes the whole layout in LDS; in FIXED
-// capacity a token block only counts the earlier pairs of its own pairs'
-// experts (its rows are e*C + that count). The first blocks copy one piece
-// (seg vectors) of one token's row each; the last ones zero-fill padding
-// rows; block 0 also writes the handle's arrays (in FIXED mode each token
-// writes its own pairs' slots and rows, block 0 the counts). A token
+// 4096, E <= 512: a few KiB read from L2 per block). Where a pair's row
+// follows from counts alone (FIXED capacity: e*C + the earlier pairs of its
+// expert; the aligned layout with alignment 1: the pairs of smaller experts
+// + the earlier pairs of its expert), a token block counts just those for its
+// own pairs; with larger alignments every block recomputes the whole layout
+// in LDS. The first blocks copy one piece (seg vectors) of one token's row
+// each; the last ones zero-fill padding rows; block 0 also writes the
+// handle's arrays (where rows follow from counts, each token writes its own
+// pairs' slots and rows and block 0 the counts and offsets). A token
 // block issues the loads of its piece of x before the layout work, so both
 // round trips overlap. Small batches have few tokens, so rows are split over
 // several blocks to reach every CU, but the grid is kept to one block per CU:

@@ -179,8 +179,8 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
  * Small batches (num_tokens * k <= 4096 and E <= 512, the decode sizes of
  * README "Example use in inference decoding") take a single kernel launch:
  * every block derives its rows from all the batch's ids (the whole small
- * layout in LDS, or in FIXED mode only the ranks of its own pairs), so no
- * block waits on another. Larger batches enqueue the layout kernels and then the dispatch
+ * layout in LDS, or, in FIXED mode and with expert_alignment 1, only the
+ * counts that place its own pairs), so no block waits on another. Larger batches enqueue the layout kernels and then the dispatch
  * kernel. Never synchronises. */
 ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
                               const float* topk_w, void* workspace, size_t workspace_bytes,
