@@ -5,8 +5,9 @@
 //
 // Token-major: one block per token (the copy itself is dispatch_token in
 // ep_dispatch_dev.h). Padding rows of the aligned layout are cleared by
-// extra blocks placed first in the grid, so they overlap with the token
-// blocks.
+// extra blocks placed first in the grid (at most kPadBlocksPerCU per CU,
+// each looping over pieces of the experts' padding), so they overlap with
+// the token blocks.
 #include "ep_internal.h"
 #include "ep_dispatch_dev.h"
 
@@ -15,12 +16,15 @@ namespace ep {
 template <int KIND>
 __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
     if ((int)blockIdx.x < a.npad_blocks) {
-        // zero-fill up to pad_rows_per_block padding rows of one expert
-        const int e = blockIdx.x / a.pad_blocks_per_expert;
-        const int part = blockIdx.x % a.pad_blocks_per_expert;
-        const int r0 = a.expert_off[e] + a.cnt[e] + part * a.pad_rows_per_block;
-        const int r1 = min(r0 + a.pad_rows_per_block, a.expert_off[e] + a.pad[e]);
-        dispatch_zero_rows<KIND>(a, r0, r1);
+        // zero-fill items blockIdx.x, + npad_blocks, ...: up to
+        // pad_rows_per_block padding rows of one expert each
+        for (int it = blockIdx.x; it < a.npad_items; it += a.npad_blocks) {
+            const int e = it / a.pad_blocks_per_expert;
+            const int part = it % a.pad_blocks_per_expert;
+            const int r0 = a.expert_off[e] + a.cnt[e] + part * a.pad_rows_per_block;
+            const int r1 = min(r0 + a.pad_rows_per_block, a.expert_off[e] + a.pad[e]);
+            dispatch_zero_rows<KIND>(a, r0, r1);
+        }
         return;
     }
     const int t = (int)blockIdx.x - a.npad_blocks;
@@ -35,7 +39,9 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
     dispatch_token<KIND>(a, t, 0, dispatch_nvec<KIND>(a), my_s, my_w);
 }
 
-hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream) {
+hipError_t launch_dispatch(int kind, const DispatchArgs& args, hipStream_t stream) {
+    DispatchArgs a = args;
+    a.npad_blocks = min(a.npad_items, kPadBlocksPerCU * device_cu_count());
     const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy || kind == kDispatchFp8QuantWeighted;
     const int nvec = fp8 ? a.H / 16 : a.H / 8;
     int threads = ((nvec + 63) / 64) * 64;

@@ -68,9 +68,10 @@ struct DispatchArgs {
     int T, H, k, E;
     int zero_pad;
     int pad_rows_max;        // most padding rows one expert can have (A - 1; 0 without zero-fill)
-    int pad_rows_per_block;  // padding rows one zero-fill block clears
-    int pad_blocks_per_expert;
-    int npad_blocks;
+    int pad_rows_per_block;  // padding rows of one zero-fill item (an expert's piece)
+    int pad_blocks_per_expert;  // zero-fill items per expert
+    int npad_items;          // zero-fill items: pad_blocks_per_expert * E
+    int npad_blocks;         // blocks that clear them (item i by block i % npad_blocks)
     // single-launch layout + dispatch only: each token's row is split into
     // nsplit blocks of seg vectors (seg <= 1024, a multiple of 8)
     int nsplit, seg;
@@ -121,22 +122,28 @@ struct GemmArgs {
     int E, K, N, mode, C;
 };
 
-// Rows of padding one zero-fill block clears: in the dispatch kernel, and in
-// the single-launch layout + dispatch, where every block also redoes the
-// small layout and so should be few. Measured on MI355X at 8192 x 7168 x
-// top-8, alignment 128 (zero-fill blocks first in the grid): 4 rows per block
-// 218-220 us for the weighted BF16 kind and 110 us for FP8 quantise, against
-// 225-228 us and 113-114 us with 16.
-constexpr int kPadRowsPerBlock = 4;
+// Padding rows per zero-fill item (a piece of one expert's padding): in the
+// dispatch kernel, and in the single-launch layout + dispatch, where every
+// block also redoes the small layout and so should be few. In the dispatch
+// kernel at most kPadBlocksPerCU blocks per CU clear the items, each looping
+// over its share, so that items past an expert's padding cost a few loads
+// instead of a launched block. Measured on MI355X at 8192 x 7168 x top-8,
+// alignment 128 (zero-fill blocks first in the grid), weighted BF16 kind:
+// 16 rows per block, one block per item 225-228 us; 4 rows 218-223 us; 2 rows
+// per item over 2,048 blocks 217.7-218.1 us (three runs in alternation).
+constexpr int kPadRowsPerBlock = 2;
+constexpr int kPadBlocksPerCU = 8;
 constexpr int kFusedPadRowsPerBlock = 16;
 
-// Sets the zero-fill grid of a dispatch: pad_blocks_per_expert blocks of
-// rows_per_block rows for each expert (blocks past an expert's padding exit).
+// Sets the zero-fill work of a dispatch: pad_blocks_per_expert items of
+// rows_per_block rows for each expert (items past an expert's padding clear
+// nothing), one block per item (launchers may cap npad_blocks).
 inline void set_pad_blocks(DispatchArgs& a, int rows_per_block) {
     a.pad_rows_per_block = rows_per_block;
     a.pad_blocks_per_expert = (a.pad_rows_max + rows_per_block - 1) / rows_per_block;
-    a.npad_blocks = a.pad_blocks_per_expert * a.E;
-    if (a.pad_blocks_per_expert == 0) a.pad_blocks_per_expert = 1;  // never divided by when npad_blocks == 0
+    a.npad_items = a.pad_blocks_per_expert * a.E;
+    a.npad_blocks = a.npad_items;
+    if (a.pad_blocks_per_expert == 0) a.pad_blocks_per_expert = 1;  // never divided by when there are no items
 }
 
 hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
