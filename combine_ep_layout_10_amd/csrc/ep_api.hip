@@ -145,7 +145,7 @@ ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, con
     a.E = c.num_experts;
     a.zero_pad = (c.mode == EP_MODE_COMPACT && !(c.flags & EP_FLAG_NO_ZERO_PAD)) ? 1 : 0;
     a.pad_rows_max = a.zero_pad ? c.expert_alignment - 1 : 0;
-    ep::set_pad_blocks(a, ep::kPadRowsPerBlock);  // the single-launch path sets its own
+    ep::set_pad_pieces(a, ep::kPadRowsPerPiece);  // the single-launch path sets its own
     if (dtype == EP_BF16)
         *kind = pair_w ? ep::kDispatchBf16Weighted : ep::kDispatchBf16;
     else if (dtype == EP_FP8_QUANTIZE)

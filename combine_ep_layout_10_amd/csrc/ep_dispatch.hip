@@ -16,13 +16,13 @@ namespace ep {
 template <int KIND>
 __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
     if ((int)blockIdx.x < a.npad_blocks) {
-        // zero-fill items blockIdx.x, + npad_blocks, ...: up to
-        // pad_rows_per_block padding rows of one expert each
-        for (int it = blockIdx.x; it < a.npad_items; it += a.npad_blocks) {
-            const int e = it / a.pad_blocks_per_expert;
-            const int part = it % a.pad_blocks_per_expert;
-            const int r0 = a.expert_off[e] + a.cnt[e] + part * a.pad_rows_per_block;
-            const int r1 = min(r0 + a.pad_rows_per_block, a.expert_off[e] + a.pad[e]);
+        // zero-fill pieces blockIdx.x, + npad_blocks, ...: up to
+        // pad_rows_per_piece padding rows of one expert each
+        for (int pc = blockIdx.x; pc < a.npad_pieces; pc += a.npad_blocks) {
+            const int e = pc / a.pad_pieces_per_expert;
+            const int part = pc % a.pad_pieces_per_expert;
+            const int r0 = a.expert_off[e] + a.cnt[e] + part * a.pad_rows_per_piece;
+            const int r1 = min(r0 + a.pad_rows_per_piece, a.expert_off[e] + a.pad[e]);
             dispatch_zero_rows<KIND>(a, r0, r1);
         }
         return;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
 
 hipError_t launch_dispatch(int kind, const DispatchArgs& args, hipStream_t stream) {
     DispatchArgs a = args;
-    a.npad_blocks = min(a.npad_items, kPadBlocksPerCU * device_cu_count());
+    a.npad_blocks = min(a.npad_pieces, kPadBlocksPerCU * device_cu_count());
     const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy || kind == kDispatchFp8QuantWeighted;
     const int nvec = fp8 ? a.H / 16 : a.H / 8;
     int threads = ((nvec + 63) / 64) * 64;

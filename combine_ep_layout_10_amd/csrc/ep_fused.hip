@@ -189,10 +189,10 @@ __global__ __launch_bounds__(1024) void k_layout_dispatch_small(LayoutArgs la, D
         if (lead && ntok == 0 && da.npad_blocks == 0) return;  // an empty batch: the handle only
         const int pb = (int)blockIdx.x - ntok;
         if (pb >= da.npad_blocks) return;
-        const int e = pb / da.pad_blocks_per_expert;
-        const int pp = pb % da.pad_blocks_per_expert;
-        const int r0 = L.s_off[e] + L.s_cnt[e] + pp * da.pad_rows_per_block;
-        const int r1 = min(r0 + da.pad_rows_per_block, L.s_off[e + 1]);
+        const int e = pb / da.pad_pieces_per_expert;
+        const int pp = pb % da.pad_pieces_per_expert;
+        const int r0 = L.s_off[e] + L.s_cnt[e] + pp * da.pad_rows_per_piece;
+        const int r1 = min(r0 + da.pad_rows_per_piece, L.s_off[e + 1]);
         dispatch_zero_rows<KIND>(da, r0, r1);
         return;
     }
@@ -223,7 +223,7 @@ bool fused_layout_dispatch_fits(int64_t pairs, int E) { return pairs <= kSmallMa
 hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& args,
                                         hipStream_t stream) {
     DispatchArgs da = args;
-    set_pad_blocks(da, kFusedPadRowsPerBlock);
+    set_pad_pieces(da, kFusedPadRowsPerPiece);
     const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy;
     const int nvec = fp8 ? da.H / 16 : da.H / 8;
     // Pieces per row: as many as keep the grid within kFusedBlocksPerCU

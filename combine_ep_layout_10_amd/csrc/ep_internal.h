@@ -68,10 +68,10 @@ struct DispatchArgs {
     int T, H, k, E;
     int zero_pad;
     int pad_rows_max;        // most padding rows one expert can have (A - 1; 0 without zero-fill)
-    int pad_rows_per_block;  // padding rows of one zero-fill item (an expert's piece)
-    int pad_blocks_per_expert;  // zero-fill items per expert
-    int npad_items;          // zero-fill items: pad_blocks_per_expert * E
-    int npad_blocks;         // blocks that clear them (item i by block i % npad_blocks)
+    int pad_rows_per_piece;     // padding rows of one zero-fill piece (of one expert's padding)
+    int pad_pieces_per_expert;  // pieces per expert
+    int npad_pieces;            // pad_pieces_per_expert * E
+    int npad_blocks;            // blocks that clear them (piece i by block i % npad_blocks)
     // single-launch layout + dispatch only: each token's row is split into
     // nsplit blocks of seg vectors (seg <= 1024, a multiple of 8)
     int nsplit, seg;
@@ -122,28 +122,28 @@ struct GemmArgs {
     int E, K, N, mode, C;
 };
 
-// Padding rows per zero-fill item (a piece of one expert's padding): in the
+// Padding rows per zero-fill piece (a piece of one expert's padding): in the
 // dispatch kernel, and in the single-launch layout + dispatch, where every
 // block also redoes the small layout and so should be few. In the dispatch
-// kernel at most kPadBlocksPerCU blocks per CU clear the items, each looping
-// over its share, so that items past an expert's padding cost a few loads
+// kernel at most kPadBlocksPerCU blocks per CU clear the pieces, each looping
+// over its share, so that pieces past an expert's padding cost a few loads
 // instead of a launched block. Measured on MI355X at 8192 x 7168 x top-8,
 // alignment 128 (zero-fill blocks first in the grid), weighted BF16 kind:
-// 16 rows per block, one block per item 225-228 us; 4 rows 218-223 us; 2 rows
-// per item over 2,048 blocks 217.7-218.1 us (three runs in alternation).
-constexpr int kPadRowsPerBlock = 2;
+// one block per 16-row piece 225-228 us; per 4-row piece 218-223 us; 2-row
+// pieces over 2,048 blocks 217.7-218.1 us (three runs in alternation).
+constexpr int kPadRowsPerPiece = 2;
 constexpr int kPadBlocksPerCU = 8;
-constexpr int kFusedPadRowsPerBlock = 16;
+constexpr int kFusedPadRowsPerPiece = 16;
 
-// Sets the zero-fill work of a dispatch: pad_blocks_per_expert items of
-// rows_per_block rows for each expert (items past an expert's padding clear
-// nothing), one block per item (launchers may cap npad_blocks).
-inline void set_pad_blocks(DispatchArgs& a, int rows_per_block) {
-    a.pad_rows_per_block = rows_per_block;
-    a.pad_blocks_per_expert = (a.pad_rows_max + rows_per_block - 1) / rows_per_block;
-    a.npad_items = a.pad_blocks_per_expert * a.E;
-    a.npad_blocks = a.npad_items;
-    if (a.pad_blocks_per_expert == 0) a.pad_blocks_per_expert = 1;  // never divided by when there are no items
+// Sets the zero-fill work of a dispatch: pad_pieces_per_expert pieces of
+// rows_per_piece rows for each expert (pieces past an expert's padding clear
+// nothing), one block per piece (launchers may cap npad_blocks).
+inline void set_pad_pieces(DispatchArgs& a, int rows_per_piece) {
+    a.pad_rows_per_piece = rows_per_piece;
+    a.pad_pieces_per_expert = (a.pad_rows_max + rows_per_piece - 1) / rows_per_piece;
+    a.npad_pieces = a.pad_pieces_per_expert * a.E;
+    a.npad_blocks = a.npad_pieces;
+    if (a.pad_pieces_per_expert == 0) a.pad_pieces_per_expert = 1;  // never divided by when there are no pieces
 }
 
 hipError_t launch_layout(const LayoutArgs& a, bool small, hipStream_t stream);
