@@ -68,6 +68,10 @@ def parse():
                    help="capture one step in a HIP graph and time K replays (launch-bound shapes)")
     p.add_argument("--bound", action="store_true",
                    help="time steps issued through bound calls (arguments converted once)")
+    p.add_argument("--rotate", type=int, default=4,
+                   help="copies of x and grad_out the eager steps cycle through (each step reads inputs no cache "
+                        "holds: 4 copies of x and grad_out are 0.94 GB at the V3 shape, against a 256 MB MALL); "
+                        "1 = the same inputs every step")
     p.add_argument("--no-flush", action="store_true",
                    help="skip the per-kernel pass with L2 and MALL flushed before each kernel")
     p.add_argument("--no-copy-ceiling", action="store_true",
@@ -191,17 +195,30 @@ def main():
         grad_x = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
         grad_w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
 
+    # The eager steps cycle through `rotate` copies of the inputs read with
+    # plain loads (x, grad_out; identical contents), so that each step reads
+    # them from HBM as a step of a real model would after other work, not
+    # from the caches the previous step left them in. The expert-output
+    # inputs (y, grad_recv: 1.4 GB each) are read with non-temporal loads and
+    # never fit the caches anyway.
+    nrot = max(1, args.rotate) if not (args.graph or args.bound) else 1
+    xs = [x] + [x.clone() for _ in range(nrot - 1)]
+    gos = ([grad_out] + [grad_out.clone() for _ in range(nrot - 1)]) if train else None
+    cur = [0]                  # the step's copy index
+
     def do_dispatch(h):
+        xi = xs[cur[0] % nrot]
         if fp8:
-            ops.dispatch(h, x, dtype, recv=recv, recv_scales=rs)
+            ops.dispatch(h, xi, dtype, recv=recv, recv_scales=rs)
         else:
-            ops.dispatch(h, x, dtype, recv=recv)
+            ops.dispatch(h, xi, dtype, recv=recv)
 
     # the calls after the layout, in step order, and the kernel each runs
     calls = {"dispatch": do_dispatch, "combine": lambda h: ops.combine(h, y, w, out=out)}
     kname = {"dispatch": "k_dispatch<2>" if fp8 else "k_dispatch<0>", "combine": "k_combine<true>"}
     if train:
-        calls["combine_backward"] = lambda h: ops.combine_backward(h, grad_out, ops.BF16, w, grad_y=grad_y)
+        calls["combine_backward"] = lambda h: ops.combine_backward(h, gos[cur[0] % nrot], ops.BF16, w,
+                                                                   grad_y=grad_y)
         calls["dispatch_backward"] = lambda h: ops.dispatch_backward(h, grad_recv, grad_row_w, grad_x=grad_x,
                                                                      grad_topk_w=grad_w)
         kname["combine_backward"] = "k_dispatch<1>"
@@ -210,9 +227,10 @@ def main():
     after = names[1:]          # what follows the layout + dispatch call
 
     def forward_head():
+        xi = xs[cur[0] % nrot]
         if fp8:
-            return ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
-        return ops.dispatch_forward(cfg, idx, x, dtype, topk_w=w, workspace=ws, recv=recv)[0]
+            return ops.dispatch_forward(cfg, idx, xi, dtype, topk_w=w, workspace=ws, recv=recv, recv_scales=rs)[0]
+        return ops.dispatch_forward(cfg, idx, xi, dtype, topk_w=w, workspace=ws, recv=recv)[0]
 
     def step():
         h = forward_head()
@@ -271,7 +289,8 @@ def main():
             step()
 
     print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        cur[0] = i
         run_step()
     torch.cuda.synchronize()
     # Timed region: exactly K steps. Eager steps carry one event pair around
@@ -290,6 +309,7 @@ def main():
             bound[0]()
             bound[1]()
             continue
+        cur[0] = args.warmup + i
         e0, e1 = dom_ev[i]
         if dominant == "dispatch":
             h = ops.layout(cfg, idx, w, workspace=ws)
@@ -316,14 +336,28 @@ def main():
     # calls with events between them (not part of the timed region).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 2)] for _ in range(args.steps)]
     for i in range(args.steps):
+        cur[0] = i
         step_split(evs[i])
     torch.cuda.synchronize()
     lay_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k_ms = {n: float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in evs])) for i, n in enumerate(names)}
     gpu_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
+    warm = None
+    if nrot > 1:
+        # the same calls on the same inputs every step (x and grad_out stay
+        # in the MALL between steps): for reference only
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 2)] for _ in range(args.steps)]
+        cur[0] = 0
+        for i in range(args.steps):
+            step_split(wev[i])
+        torch.cuda.synchronize()
+        warm = {n + "_us": round(float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in wev])) * 1e3, 2)
+                for i, n in enumerate(names)}
+        warm["stat"] = "mean of %d steps on one copy of the inputs" % args.steps
     # the step with dispatch_forward as one unit (one launch for small batches)
     fw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1 in fw:
+    for i, (e0, e1) in enumerate(fw):
+        cur[0] = i
         e0.record(stream)
         step()
         e1.record(stream)
@@ -340,7 +374,9 @@ def main():
                 "kernel": kname[dominant], "call": dominant,
                 "algorithmic_bytes_per_launch": nbytes[dominant],
                 "avg_launch_us": round(dom_ms * 1e3, 2),
-                "timed": "events in the timed region" if dom_live_ms is not None else "evented eager pass"}
+                "timed": "events in the timed region" if dom_live_ms is not None else "evented eager pass",
+                "inputs": ("x and grad_out cycled through %d copies (read from HBM, not from the caches)" % nrot
+                           if nrot > 1 else "the same inputs every step")}
 
     flushed = None
     if not args.no_flush and graph is None and bound is None:
@@ -358,6 +394,7 @@ def main():
             torch.sum(scratch.view(torch.int32), dim=0, out=sink)
 
         fl = []
+        cur[0] = 0
         for i in range(args.steps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (len(names) + 1))]
             flush(i & 0x7F)
@@ -444,7 +481,7 @@ def main():
         kernels[n + "_GBps"] = round(gbps[n], 1)
         kernels[n + "_frac"] = round(gbps[n] / HBM_PEAK_GBPS, 4)
     kernels.update({"bytes": nbytes, "kernel_bytes": {kname[n]: nbytes[n] for n in names}, "kernel_hash": khash,
-                    "cold_cache": flushed, "copy_1GiB_GBps": copy_ceiling,
+                    "cold_cache": flushed, "warm": warm, "copy_1GiB_GBps": copy_ceiling,
                     "fill_1GiB_GBps": fill_ceiling})
     # the dominant kernel against the rates measured in this run (a device
     # copy: half reads, half writes; a fill: writes only)

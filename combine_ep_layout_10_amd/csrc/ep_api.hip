@@ -2,6 +2,7 @@
 // workspace map, handle construction and kernel launches on the caller's
 // stream. No device memory is allocated here.
 #include <stdarg.h>
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -265,16 +266,21 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
 
 namespace ep {
 
-int device_cu_count() {
-    static int cached[64] = {0};
+hipError_t device_cu_count(int* out) {
+    static std::atomic<int> cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (n <= 0) return hipErrorInvalidDevice;
+        cached[dev].store(n, std::memory_order_relaxed);  // every thread stores the same value
     }
-    return cached[dev];
+    *out = n;
+    return hipSuccess;
 }
 
 }  // namespace ep

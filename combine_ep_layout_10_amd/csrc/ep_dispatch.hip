@@ -41,7 +41,10 @@ __global__ __launch_bounds__(1024) void k_dispatch(DispatchArgs a) {
 
 hipError_t launch_dispatch(int kind, const DispatchArgs& args, hipStream_t stream) {
     DispatchArgs a = args;
-    a.npad_blocks = min(a.npad_pieces, kPadBlocksPerCU * device_cu_count());
+    int cus = 0;
+    const hipError_t err = device_cu_count(&cus);
+    if (err != hipSuccess) return err;
+    a.npad_blocks = min(a.npad_pieces, kPadBlocksPerCU * cus);
     const bool fp8 = kind == kDispatchFp8Quant || kind == kDispatchFp8Copy || kind == kDispatchFp8QuantWeighted;
     const int nvec = fp8 ? a.H / 16 : a.H / 8;
     int threads = ((nvec + 63) / 64) * 64;

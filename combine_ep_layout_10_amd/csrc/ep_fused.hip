@@ -229,7 +229,10 @@ hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const Di
     // Pieces per row: as many as keep the grid within kFusedBlocksPerCU
     // blocks per CU (padding blocks included), at least 64 vectors per
     // piece, at most 1024 (one vector per thread).
-    const int resident = kFusedBlocksPerCU * device_cu_count();
+    int cus = 0;
+    hipError_t err = device_cu_count(&cus);
+    if (err != hipSuccess) return err;
+    const int resident = kFusedBlocksPerCU * cus;
     int nsplit = da.T > 0 ? max(1, (resident - da.npad_blocks) / da.T) : 1;
     nsplit = min(nsplit, (nvec + 63) / 64);
     nsplit = max(nsplit, (nvec + 1023) / 1024);

@@ -99,8 +99,10 @@ constexpr int kCombineSegLarge = 128;
 // its SIMDs (measured on MI355X at 128 x 7168 x top-8: one block per CU,
 // two pieces per row, beats two blocks per CU by about 4 us).
 constexpr int kFusedBlocksPerCU = 1;
-// Compute units of the current device (queried once per device).
-int device_cu_count();
+// Compute units of the current device (queried once per device; the cache is
+// atomic, so concurrent first calls are safe). Returns the failed query's
+// error instead of guessing a count.
+hipError_t device_cu_count(int* out);
 
 struct WeightGradArgs {
     const uint16_t* grad_out;
