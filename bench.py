@@ -19,8 +19,9 @@ write) over time; `roofline` reports the kernel that moves the most bytes
 against the MI355X HBM peak, timed with HIP events recorded around it
 inside the timed region, on the stream the kernels run on (--graph replays a
 captured step instead; the per-kernel times then come from an evented eager
-pass). `cpu_baseline` times the single-threaded CPU oracle on the same inputs
-and the same work.
+pass). `cpu_baseline` times the CPU oracle on the same inputs and the same
+work: its OpenMP build on the host's cores (the value) and its plain build on
+one core (`single_core`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--step path|forward] [--graph | --bound]
     python bench.py --step gemm [--gemm-n 4096]   # the FP8 grouped GEMM on the receive layout
@@ -137,6 +138,47 @@ def load_traffic(kernel: str, khash: str, workload: str, path: str = None):
     if not ent or ent.get("kernel_hash") != khash or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
+
+
+def host_threads() -> int:
+    """Host threads for the oracle's OpenMP leg: the cores this process may
+    run on, capped by OMP_NUM_THREADS when the environment sets it."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def time_oracle(run, budget_s: float, max_runs: int = 50):
+    """Median wall time of run() over at least one and at most max_runs
+    calls, stopping once budget_s has passed; returns (seconds, runs)."""
+    import numpy as np
+    times = []
+    end = time.perf_counter() + budget_s
+    while not times or (len(times) < max_runs and time.perf_counter() < end):
+        c0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - c0)
+        print("[bench] oracle run %.2f s" % times[-1], file=sys.stderr, flush=True)
+    return float(np.median(times)), len(times)
+
+
+def oracle_baseline(run, nbytes: float, unit_scale: float, unit: str, budget_s: float, what: str) -> dict:
+    """The oracle timed twice on the same work: the OpenMP build on this
+    host's cores (the reported value) and the plain build on one core. The
+    layout inside `run` stays serial in both."""
+    import oracle
+    n = oracle.threads(host_threads())
+    t_mt, k_mt = time_oracle(run, budget_s / 3)
+    oracle.threads(0)
+    t_1, k_1 = time_oracle(run, budget_s * 2 / 3)
+    return {"value": round(nbytes / t_mt / unit_scale, 6 if unit == "TFLOP/s" else 3), "unit": unit, "cores": n,
+            "kind": "oracle",
+            "sample": "%s; C oracle, OpenMP over tokens on %d host threads (layout serial): median of %d runs of "
+                      "%.3f s; single-threaded: median of %d runs of %.2f s" % (what, n, k_mt, t_mt, k_1, t_1),
+            "single_core": {"value": round(nbytes / t_1 / unit_scale, 6 if unit == "TFLOP/s" else 3),
+                            "unit": unit, "cores": 1}}
 
 
 def main():
@@ -450,10 +492,7 @@ def main():
             go_h = grad_out.view(torch.int16).cpu().numpy().view(np.uint16)
             gr_h = grad_recv.view(torch.int16).cpu().numpy().view(np.uint16)
             grw_h = grad_row_w.cpu().numpy()
-        times = []
-        budget_end = time.perf_counter() + args.cpu_budget_s
-        while not times or (len(times) < 3 and time.perf_counter() < budget_end):
-            c0 = time.perf_counter()
+        def run():
             lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, idx_h, w_h)
             if fp8:
                 oracle.dispatch_fp8(lay, x_h, wl.k)
@@ -463,14 +502,10 @@ def main():
             if train:
                 oracle.combine_backward_bf16(lay, go_h, wl.k, w_h)
                 oracle.dispatch_backward(lay, gr_h, wl.k, grw_h)
-            times.append(time.perf_counter() - c0)
-            print("[bench] oracle step %.2f s" % times[-1], file=sys.stderr, flush=True)
-        cpu_s = float(np.median(times))
-        cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "the full %s step (layout + %s dispatch + combine%s) on the same inputs, median of %d "
-                         "runs of %.2f s; single-threaded C oracle"
-                         % (wl.name, wl.dispatch, " + combine_backward + dispatch_backward" if train else "",
-                            len(times), cpu_s)}
+
+        cpu = oracle_baseline(run, step_bytes, 1e9, "GB/s", args.cpu_budget_s,
+                              "the full %s step (layout + %s dispatch + combine%s) on the same inputs"
+                              % (wl.name, wl.dispatch, " + combine_backward + dispatch_backward" if train else ""))
 
     kernels = {"layout_us": round(lay_ms * 1e3, 2)}
     for n in names:
@@ -587,16 +622,8 @@ def bench_call(args):
             run = lambda: oracle.combine_weight_grad(lay, go_h, y_h, wl.k)
         else:
             run = lambda: oracle.combine_backward_fp8(lay, go_h, wl.k, w_h)
-        times = []
-        budget_end = time.perf_counter() + args.cpu_budget_s
-        while not times or (len(times) < 3 and time.perf_counter() < budget_end):
-            c0 = time.perf_counter()
-            run()
-            times.append(time.perf_counter() - c0)
-        cpu_s = float(np.median(times))
-        cpu = {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "the same %s call on the same inputs, median of %d runs of %.2f s; single-threaded "
-                         "C oracle" % (what, len(times), cpu_s)}
+        cpu = oracle_baseline(run, nbytes, 1e9, "GB/s", args.cpu_budget_s,
+                              "the same %s call on the same inputs" % what)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -676,28 +703,31 @@ def bench_gemm(args):
         qh, sh = q.cpu().numpy(), s.cpu().numpy()
         off = h.expert_off.cpu().numpy()
         rng = np.random.default_rng(0)
-        samples = []                              # inputs copied to the host before the timed loop
-        for _ in range(64):
+        # 64 random routed rows, each with one random 128-channel piece of its
+        # expert's weights, packed as a grouped GEMM of 64 one-row experts
+        # (inputs copied to the host before the timed runs)
+        ns = 64
+        a1 = np.zeros((ns, H), np.uint8)
+        s1 = np.zeros((ns, H // 128), np.float32)
+        b1 = np.zeros((ns, 128, H), np.uint8)
+        sb1 = np.zeros((ns, 1, H // 128), np.float32)
+        for i in range(ns):
             r = int(rng.integers(0, int(off[-1])))
             n0 = int(rng.integers(0, N // 128)) * 128
             e = int(np.searchsorted(off, r, side="right") - 1)
-            a1 = np.zeros((128, H), np.uint8)
-            a1[0] = qh[r]
-            s1 = np.zeros((128, H // 128), np.float32)
-            s1[0] = sh[r]
-            samples.append((a1, s1, b[e:e + 1, n0:n0 + 128].cpu().numpy(),
-                            sb[e:e + 1, n0 // 128:n0 // 128 + 1].cpu().numpy()))
-        rb, re_ = np.array([0], np.int32), np.array([1], np.int32)
-        m = 0
-        c0 = time.perf_counter()
-        while time.perf_counter() - c0 < args.cpu_budget_s / 2:
-            a1, s1, b1, sb1 = samples[(m // 128) % len(samples)]
-            oracle.grouped_gemm_fp8(rb, re_, a1, s1, b1, sb1)
-            m += 128
-        cpu_s = time.perf_counter() - c0
-        cpu = {"value": round(2.0 * m * H / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-               "sample": "%d outputs (128-channel pieces of 64 random rows) of the same GEMM in %.1f s, "
-                         "single-threaded C oracle in binary64" % (m, cpu_s)}
+            a1[i], s1[i] = qh[r], sh[r]
+            b1[i] = b[e, n0:n0 + 128].cpu().numpy()
+            sb1[i, 0] = sb[e, n0 // 128].cpu().numpy()
+        rb = np.arange(ns, dtype=np.int32)
+        re_ = rb + 1
+        pairs_ = np.stack([np.repeat(np.arange(ns), 128), np.tile(np.arange(128), ns)], axis=1).astype(np.int64)
+
+        def run():
+            oracle.grouped_gemm_fp8(rb, re_, a1, s1, b1, sb1, pairs=pairs_)
+
+        cpu = oracle_baseline(run, 2.0 * len(pairs_) * H, 1e12, "TFLOP/s", args.cpu_budget_s,
+                              "%d outputs (128-channel pieces of %d random routed rows) of the same GEMM in "
+                              "binary64" % (len(pairs_), ns))
     kname = "k_grouped_gemm_fp8_dma" if N % 256 == 0 and H // 128 <= 256 else "k_grouped_gemm_fp8"
     # the least HBM traffic of one launch: weights and A rows (with scales)
     # read once, the output rows written once

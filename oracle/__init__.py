@@ -8,7 +8,10 @@ The arithmetic lives in ``ep_oracle.c`` (plain single-threaded C, built with
 gcc -O2 -ffp-contract=off). This module compiles it on first use when the
 shared object is missing or older than the source, and marshals numpy arrays
 through ctypes. Every function here states the reading it follows; the C
-file cites the page passages.
+file cites the page passages. A second build of the same file with -fopenmp
+spreads the per-token loops over host threads (``threads(n)`` selects it for
+the calls that follow); it exists to time the oracle on several cores and
+returns the same bits as the plain build.
 
 Parity pins: every function is pinned by tests under ``tests/`` against
 closed forms, library special cases, brute force and hand-derived fixtures;
@@ -26,31 +29,54 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
 _LIB = os.path.join(_HERE, "libep_oracle.so")
+_LIB_OMP = os.path.join(_HERE, "libep_oracle_omp.so")
 
 MODE_COMPACT = 0
 MODE_FIXED = 1
 FLAG_BAD_ID = 1
 FLAG_OVERFLOW = 2
 
-_lib = None
+_libs = {}
+_use_omp = False
+
+
+def _build_one(out: str, omp: bool, force: bool) -> str:
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+               "-Wall", "-Wextra", "-shared", "-fPIC"]
+        cmd += ["-fopenmp"] if omp else ["-Wno-unknown-pragmas"]
+        cmd += ["-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
-               "-Wall", "-Wextra", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+    """Compile the oracle with gcc (no fast-math, no contraction): the plain
+    build and the OpenMP timing build of the same source."""
+    _build_one(_LIB_OMP, True, force)
+    return _build_one(_LIB, False, force)
+
+
+def threads(n: int) -> int:
+    """Route the calls that follow through the OpenMP build with n threads
+    (n >= 1), or back to the plain build (n = 0). Returns the threads the
+    loops use (1 for the plain build)."""
+    global _use_omp
+    _use_omp = n > 0
+    return int(_load().ora_threads(n))
 
 
 def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    lib = ctypes.CDLL(build())
+    key = "omp" if _use_omp else "plain"
+    lib = _libs.get(key)
+    if lib is not None:
+        return lib
+    path = _build_one(_LIB_OMP, True, False) if _use_omp else build()
+    lib = ctypes.CDLL(path)
+    lib.ora_threads.restype = ctypes.c_int
+    lib.ora_threads.argtypes = [ctypes.c_int]
     P = ctypes.c_void_p
     i32 = ctypes.c_int
     lib.ora_layout.restype = ctypes.c_uint32
@@ -79,7 +105,7 @@ def _load():
     lib.ora_e4m3_code_value.argtypes = [i32]
     lib.ora_quantize_block.restype = ctypes.c_float
     lib.ora_quantize_block.argtypes = [P, i32, P]
-    _lib = lib
+    _libs[key] = lib
     return lib
 
 

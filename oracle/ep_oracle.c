@@ -35,10 +35,18 @@
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC -lm
  * (no -march flags: no vector or fused code that would alter rounding).
+ * The per-token loops carry OpenMP work-sharing pragmas, used only by a
+ * second build of this same file (-fopenmp) that times the oracle on several
+ * host cores. Tokens are independent, every (token, k) pair writes its own
+ * receive row, and nothing inside a token's computation changes order, so
+ * both builds give the same bits; the plain build ignores the pragmas.
  */
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORA_MODE_COMPACT 0
 #define ORA_MODE_FIXED 1
@@ -267,6 +275,7 @@ void ora_dispatch_bf16(int T, int H, int k, int E, const uint16_t* x,
                        const int32_t* slot, const float* pair_w,
                        const int32_t* cnt, const int32_t* pad, const int32_t* expert_off,
                        int zero_pad, uint16_t* recv) {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int j = 0; j < k; ++j) {
             int32_t s = slot[(int64_t)t * k + j];
@@ -281,6 +290,7 @@ void ora_dispatch_bf16(int T, int H, int k, int E, const uint16_t* x,
         }
     }
     if (zero_pad) {
+#pragma omp parallel for schedule(static)
         for (int e = 0; e < E; ++e)
             for (int32_t r = ora_pad_begin(cnt, expert_off, e); r < expert_off[e] + pad[e]; ++r)
                 for (int h = 0; h < H; ++h)
@@ -321,8 +331,9 @@ void ora_dispatch_fp8(int T, int H, int k, int E, const uint16_t* x, const int32
                       const int32_t* cnt, const int32_t* pad, const int32_t* expert_off,
                       int zero_pad, uint8_t* recv, float* recv_scales) {
     int nb = H / 128;
-    uint8_t q[128];
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
+        uint8_t q[128];
         for (int b = 0; b < nb; ++b) {
             float s = ora_quantize_block(x + (int64_t)t * H + (int64_t)b * 128, 128, q);
             for (int j = 0; j < k; ++j) {
@@ -335,6 +346,7 @@ void ora_dispatch_fp8(int T, int H, int k, int E, const uint16_t* x, const int32
         }
     }
     if (zero_pad) {
+#pragma omp parallel for schedule(static)
         for (int e = 0; e < E; ++e)
             for (int32_t r = ora_pad_begin(cnt, expert_off, e); r < expert_off[e] + pad[e]; ++r) {
                 memset(recv + (int64_t)r * H, 0, (size_t)H);
@@ -355,9 +367,10 @@ void ora_combine_backward_fp8(int T, int H, int k, int E, const uint16_t* g, con
                               const int32_t* slot, const int32_t* cnt, const int32_t* pad,
                               const int32_t* expert_off, int zero_pad, uint8_t* recv, float* recv_scales) {
     int nb = H / 128;
-    uint16_t row[128];
-    uint8_t q[128];
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
+        uint16_t row[128];
+        uint8_t q[128];
         for (int j = 0; j < k; ++j) {
             int32_t r = slot[(int64_t)t * k + j];
             if (r < 0)
@@ -372,6 +385,7 @@ void ora_combine_backward_fp8(int T, int H, int k, int E, const uint16_t* g, con
         }
     }
     if (zero_pad) {
+#pragma omp parallel for schedule(static)
         for (int e = 0; e < E; ++e)
             for (int32_t r = ora_pad_begin(cnt, expert_off, e); r < expert_off[e] + pad[e]; ++r) {
                 memset(recv + (int64_t)r * H, 0, (size_t)H);
@@ -388,6 +402,7 @@ void ora_dispatch_fp8_prequant(int T, int H, int k, int E, const uint8_t* xq, co
                                const int32_t* expert_off, int zero_pad,
                                uint8_t* recv, float* recv_scales) {
     int nb = H / 128;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int j = 0; j < k; ++j) {
             int32_t r = slot[(int64_t)t * k + j];
@@ -398,6 +413,7 @@ void ora_dispatch_fp8_prequant(int T, int H, int k, int E, const uint8_t* xq, co
         }
     }
     if (zero_pad) {
+#pragma omp parallel for schedule(static)
         for (int e = 0; e < E; ++e)
             for (int32_t r = ora_pad_begin(cnt, expert_off, e); r < expert_off[e] + pad[e]; ++r) {
                 memset(recv + (int64_t)r * H, 0, (size_t)H);
@@ -420,6 +436,7 @@ void ora_dispatch_fp8_prequant(int T, int H, int k, int E, const uint8_t* xq, co
  * received weight gradients. */
 void ora_combine(int T, int H, int k, const uint16_t* y, const int32_t* slot,
                  const float* w, uint16_t* out, const float* row_vals, float* out_vals) {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int h = 0; h < H; ++h) {
             float acc = 0.0f;
@@ -457,6 +474,7 @@ void ora_combine(int T, int H, int k, const uint16_t* y, const int32_t* slot,
  * h = 0..H-1. */
 void ora_combine_weight_grad(int T, int H, int k, const uint16_t* grad_out, const uint16_t* y,
                              const int32_t* slot, double* grad_w) {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int j = 0; j < k; ++j) {
             int32_t s = slot[(int64_t)t * k + j];
@@ -542,6 +560,7 @@ void ora_grouped_gemm_fp8(int E, int K, int N, const int32_t* row_begin, const i
 void ora_grouped_gemm_fp8_at(int E, int K, int N, const int32_t* row_begin, const int32_t* row_end,
                              const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                              const int64_t* pairs, int64_t n_pairs, uint16_t* out) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n_pairs; ++i) {
         int64_t r = pairs[2 * i], n = pairs[2 * i + 1];
         int e = 0;
@@ -560,4 +579,17 @@ void ora_e4m3_encode_many(const float* v, int64_t n, uint8_t* q) {
 void ora_bf16_rne_many(const float* v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i)
         out[i] = ora_bf16_rne(v[i]);
+}
+
+/* Threads the OpenMP build's loops use (n > 0 sets them); 1 in the plain
+ * build, whose loops run on the calling thread. */
+int ora_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
 }

@@ -120,3 +120,36 @@ def test_traffic_only_for_the_measured_workload_and_sources(tmp_path):
     assert bench.load_traffic("k_combine<true>", "abd", "v3", str(p)) is None
     assert bench.load_traffic("k_combine<false>", "abc", "v3", str(p)) is None
     assert bench.load_traffic("k_combine<true>", "abc", "v3", str(tmp_path / "missing.json")) is None
+
+
+def test_host_threads_respects_affinity_and_cap(monkeypatch):
+    n_aff = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.host_threads() == n_aff
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    assert bench.host_threads() == min(2, n_aff)
+    monkeypatch.setenv("OMP_NUM_THREADS", "junk")
+    assert bench.host_threads() == n_aff
+
+
+def test_oracle_baseline_reports_threads_and_single_core(monkeypatch):
+    """Both legs run the same work; `cores` is the thread count the OpenMP
+    build reports, the plain build's figure sits under single_core."""
+    import numpy as np
+    import oracle
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    wl = WORKLOADS["tiny"]
+    from ep_workloads import make_inputs
+    inp = make_inputs(wl)
+    lay = oracle.layout(wl.mode, wl.T, wl.E, wl.k, wl.A, wl.D, wl.C, inp["topk_idx"], inp["topk_w"])
+    seen = []
+
+    def run():
+        seen.append(oracle.combine(lay, inp["y"], wl.k, inp["topk_w"])[0])
+
+    res = bench.oracle_baseline(run, 1e6, 1e9, "GB/s", 0.2, "tiny combine")
+    assert res["cores"] == min(2, len(os.sched_getaffinity(0)))
+    assert res["single_core"]["cores"] == 1
+    assert res["value"] > 0 and res["single_core"]["value"] > 0
+    assert all(np.array_equal(seen[0], s) for s in seen)
+    assert oracle.threads(0) == 1
