@@ -59,6 +59,7 @@ class ep_handle(ctypes.Structure):
         ("row_w", ctypes.c_void_p),
         ("err_flags", ctypes.c_void_p),
         ("internal", ctypes.c_void_p),
+        ("topk_idx", ctypes.c_void_p),
     ]
 
 

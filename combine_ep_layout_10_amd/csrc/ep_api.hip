@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <atomic>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "ep_internal.h"
@@ -222,6 +223,7 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
     h.row_src = (int32_t*)(ws + m.rsrc);
     h.row_w = (float*)(ws + m.rw);
     h.internal = ws + m.bpart;
+    h.topk_idx = num_tokens > 0 ? topk_idx : nullptr;
 
     const int64_t P = (int64_t)num_tokens * cfg->num_topk;
     const bool small = P <= ep::kSmallMaxPairs && cfg->num_experts <= ep::kSmallMaxExperts;
@@ -266,7 +268,36 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
 
 namespace ep {
 
+namespace {
+
+// A positive integer from the environment, or 0 when unset or malformed.
+int env_int(const char* name) {
+    const char* v = getenv(name);
+    if (v == nullptr || *v == 0) return 0;
+    char* end = nullptr;
+    const long n = strtol(v, &end, 10);
+    return (*end == 0 && n > 0 && n <= (1 << 30)) ? (int)n : 0;
+}
+
+}  // namespace
+
+bool launch_debug() { return env_int("EP_BUFFER_DEBUG") == 1; }
+
+void launch_debug_print(const char* kernel, dim3 grid, dim3 block, const char* fmt, ...) {
+    char extra[256] = "";
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(extra, sizeof extra, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[ep] %s grid %u block %u %s\n", kernel, grid.x, block.x, extra);
+}
+
 hipError_t device_cu_count(int* out) {
+    const int forced = env_int("EP_LAUNCH_CUS");
+    if (forced >= 1 && forced <= 4096) {
+        *out = forced;
+        return hipSuccess;
+    }
     static std::atomic<int> cached[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

@@ -147,6 +147,7 @@ hipError_t launch_weight_grad(const WeightGradArgs& a, hipStream_t stream) {
     const int nvec = a.H / 8;
     int threads = ((nvec + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
+    if (launch_debug()) launch_debug_print("k_weight_grad", dim3(a.T), dim3(threads), "tokens %d", a.T);
     hipLaunchKernelGGL(k_weight_grad, dim3(a.T), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
@@ -155,20 +156,26 @@ hipError_t launch_combine(const CombineArgs& args, hipStream_t stream) {
     if (args.T == 0) return hipSuccess;
     CombineArgs a = args;
     const int nvec = a.H / 8;
+    int cus = 0;
+    const hipError_t err = device_cu_count(&cus);
+    if (err != hipSuccess) return err;
+    const int target = kSplitBlocksPerCU * cus;
     // Batches with fewer tokens than about two per CU split each row into
     // pieces of at least 64 vectors, so that the gather reaches every CU.
     // Larger batches split rows into pieces of about kCombineSegLarge
     // vectors: small blocks refill the CUs' wave slots sooner than one
     // block per row (measured on MI355X at 8192 x 7168 x top-8: 128-thread
     // blocks 179 us against 184 us for 896-thread blocks).
-    int nsplit = a.T < kSplitTargetBlocks ? (kSplitTargetBlocks + a.T - 1) / a.T
-                                          : (nvec + kCombineSegLarge - 1) / kCombineSegLarge;
+    int nsplit = a.T < target ? (target + a.T - 1) / a.T : (nvec + kCombineSegLarge - 1) / kCombineSegLarge;
     nsplit = max(1, min(nsplit, nvec / 64));
     a.seg = (nvec + nsplit - 1) / nsplit;
     a.nsplit = (nvec + a.seg - 1) / a.seg;
     int threads = ((a.seg + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
     const dim3 grid((unsigned)a.T * a.nsplit);
+    if (launch_debug())
+        launch_debug_print(a.w != nullptr ? "k_combine<true>" : "k_combine<false>", grid, dim3(threads),
+                           "tokens %d pieces/row %d vectors/piece %d", a.T, a.nsplit, a.seg);
     if (a.w != nullptr)
         hipLaunchKernelGGL(k_combine<true>, grid, dim3(threads), 0, stream, a);
     else

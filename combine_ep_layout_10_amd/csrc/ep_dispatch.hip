@@ -54,6 +54,10 @@ hipError_t launch_dispatch(int kind, const DispatchArgs& args, hipStream_t strea
     if (grid64 == 0) return hipSuccess;
     if (grid64 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int grid = (int)grid64;
+    if (launch_debug())
+        launch_debug_print("k_dispatch", dim3(grid), dim3(threads),
+                           "kind %d tokens %d zero-fill blocks %d pieces %d rows/piece %d", kind, a.T, a.npad_blocks,
+                           a.npad_pieces, a.pad_rows_per_piece);
     switch (kind) {
         case kDispatchBf16:
             hipLaunchKernelGGL(k_dispatch<kDispatchBf16>, dim3(grid), dim3(threads), 0, stream, a);

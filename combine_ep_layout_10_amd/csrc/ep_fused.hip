@@ -244,6 +244,10 @@ hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const Di
     int grid = da.T * da.nsplit + da.npad_blocks;
     if (grid == 0) grid = 1;  // the handle of an empty batch is still written
     const size_t lds = small_layout_lds_bytes(la.E, la.D);
+    if (launch_debug())
+        launch_debug_print("k_layout_dispatch_small", dim3(grid), dim3(1024),
+                           "kind %d tokens %d pieces/row %d vectors/piece %d zero-fill blocks %d", kind, da.T,
+                           da.nsplit, da.seg, da.npad_blocks);
     switch (kind) {
         case kDispatchBf16: launch_fused_kind<kDispatchBf16>(la, da, grid, lds, stream); break;
         case kDispatchFp8Quant: launch_fused_kind<kDispatchFp8Quant>(la, da, grid, lds, stream); break;

@@ -528,6 +528,9 @@ hipError_t launch_grouped_gemm_fp8(const GemmArgs& a, int64_t rows_bound, hipStr
         blocks = (int64_t)a.E * (a.C / kTile) * nt_n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (launch_debug())
+        launch_debug_print(wide ? "k_grouped_gemm_fp8_dma" : "k_grouped_gemm_fp8", dim3((unsigned)blocks),
+                           dim3(wide ? 512 : 256), "n %d hidden %d", a.N, a.K);
     if (wide)
         hipLaunchKernelGGL(k_grouped_gemm_fp8_dma, dim3((unsigned)blocks), dim3(512), 0, stream, a);
     else

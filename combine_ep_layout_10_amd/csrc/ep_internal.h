@@ -88,21 +88,25 @@ struct CombineArgs {
     int nsplit, seg;  // each token's row is split into nsplit blocks of seg vectors
 };
 
-// Combine splits the rows of batches smaller than this many tokens so that
-// about this many blocks gather.
-constexpr int kSplitTargetBlocks = 512;
+// Combine splits the rows of batches smaller than this many tokens per CU so
+// that about this many blocks per CU gather.
+constexpr int kSplitBlocksPerCU = 2;
 // Vectors per block piece of the combine for batches of at least
-// kSplitTargetBlocks tokens.
+// kSplitBlocksPerCU tokens per CU.
 constexpr int kCombineSegLarge = 128;
 // Blocks of the single-launch layout + dispatch per CU. Every block redoes
 // the small layout, so a second block on a CU competes with the first for
 // its SIMDs (measured on MI355X at 128 x 7168 x top-8: one block per CU,
 // two pieces per row, beats two blocks per CU by about 4 us).
 constexpr int kFusedBlocksPerCU = 1;
-// Compute units of the current device (queried once per device; the cache is
-// atomic, so concurrent first calls are safe). Returns the failed query's
-// error instead of guessing a count.
+// Compute units the launchers size grids for: the current device's count
+// (queried once per device; the cache is atomic, so concurrent first calls
+// are safe), or EP_LAUNCH_CUS when the environment sets it to 1..4096.
+// Returns the failed query's error instead of guessing a count.
 hipError_t device_cu_count(int* out);
+// EP_BUFFER_DEBUG=1: launchers print the geometry they pick to stderr.
+bool launch_debug();
+void launch_debug_print(const char* kernel, dim3 grid, dim3 block, const char* fmt, ...);
 
 struct WeightGradArgs {
     const uint16_t* grad_out;

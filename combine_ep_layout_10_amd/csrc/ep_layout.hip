@@ -305,6 +305,7 @@ hipError_t launch_layout(const LayoutArgs& args, bool small, hipStream_t stream)
     if (small) {
         const int P = a.T * a.k;
         const size_t lds = small_layout_lds_bytes(a.E, a.D);
+        if (launch_debug()) launch_debug_print("k_layout_small", dim3(1), dim3(1024), "pairs %d", P);
         if (P <= 1024)
             hipLaunchKernelGGL(k_layout_small<1>, dim3(1), dim3(1024), lds, stream, a);
         else
@@ -319,6 +320,10 @@ hipError_t launch_layout(const LayoutArgs& args, bool small, hipStream_t stream)
     // one-block scan caches at most 16 partials per thread, so it stops there)
     a.tpe = 1;
     while ((inline_scan || a.tpe < 16) && (a.tpe * 2) * a.E <= 1024) a.tpe *= 2;
+    if (launch_debug())
+        launch_debug_print("k_layout_count+assign", dim3(a.nblk), dim3(kLayoutWaves * 64),
+                           "pairs %lld scan %s threads/expert %d", (long long)a.T * a.k,
+                           inline_scan ? "inline" : "one-block", a.tpe);
     hipLaunchKernelGGL(k_layout_count, dim3(a.nblk), dim3(kLayoutWaves * 64), lds_count, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -97,12 +97,22 @@ def _need(t: Optional[torch.Tensor], shape, name: str) -> None:
 
 
 class Handle:
-    """An ep_handle plus the workspace tensor it points into."""
+    """An ep_handle plus the workspace tensor it points into and the topk_idx
+    tensor the layout was built from (README "Example use in inference
+    decoding": a cached handle hands back its topk_idx)."""
 
-    def __init__(self, cfg: Config, h: F.ep_handle, workspace: torch.Tensor):
+    def __init__(self, cfg: Config, h: F.ep_handle, workspace: torch.Tensor,
+                 topk_idx: Optional[torch.Tensor] = None):
         self.cfg = cfg
         self.c = h
         self.workspace = workspace
+        self._topk_idx = topk_idx
+
+    @property
+    def topk_idx(self) -> Optional[torch.Tensor]:
+        """The [T, k] routing tensor of this layout (the caller's tensor, not
+        a copy; ep_handle.topk_idx points at it)."""
+        return self._topk_idx
 
     @property
     def num_tokens(self) -> int:
@@ -189,7 +199,7 @@ def layout(cfg: Config, topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor] =
         workspace = new_workspace(cfg, topk_idx.device)
     h = F.ep_layout(_c_config(cfg), T, _dev(topk_idx, "topk_idx", idx_dtype), _opt(topk_w, "topk_w", torch.float32),
                     _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
-    return Handle(cfg, h, workspace)
+    return Handle(cfg, h, workspace, topk_idx)
 
 
 def _recv_buffers(h: Handle, dtype: int, device, recv, recv_scales):
@@ -252,7 +262,7 @@ def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype
                               workspace.numel(), dtype, _dev(x, "x", xdt), _opt(x_scales, "x_scales", torch.float32),
                               _dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16),
                               _opt(recv_scales, "recv_scales", torch.float32), _stream())
-    h = Handle(cfg, c, workspace)
+    h = Handle(cfg, c, workspace, topk_idx)
     return (h, recv, recv_scales) if fp8 else (h, recv)
 
 
@@ -401,7 +411,7 @@ def bind_dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, 
     call = BoundCall(F.lib().ep_dispatch_forward, args, "ep_dispatch_forward",
                      (cfg, c, hc, topk_idx, topk_w, x, x_scales, recv, recv_scales, workspace))
     call()
-    return call, Handle(cfg, hc, workspace)
+    return call, Handle(cfg, hc, workspace, topk_idx)
 
 
 def bind_combine(h: Handle, y: torch.Tensor, out: torch.Tensor, topk_w: Optional[torch.Tensor] = None):

@@ -40,6 +40,16 @@
  *     aligned; hidden must be a multiple of 8 (BF16) or 128 (FP8).
  *   - Numbers: bf16 = bfloat16 bit patterns (uint16); FP8 = OCP E4M3FN bytes;
  *     scales and weights are IEEE binary32.
+ *   - Environment (read at each launch):
+ *       EP_BUFFER_DEBUG=1  print, to stderr, the launch geometry each call
+ *                          picks (kernel, grid, block, rows per zero-fill
+ *                          piece, row pieces per token): the library's form
+ *                          of the README's EP_BUFFER_DEBUG (section
+ *                          "Environment variables": print buffer set-up and
+ *                          SM-count choices).
+ *       EP_LAUNCH_CUS=n    size grids as if the device had n compute units
+ *                          (1 <= n <= 4096). Results never depend on launch
+ *                          geometry; this knob exists so tests can show it.
  */
 #ifndef EP_H
 #define EP_H
@@ -128,7 +138,12 @@ typedef struct {
  *                  (COMPACT); FIXED rows past pad[e] are not written
  *   row_w[Rcap]    topk_w of the pair held by each row, 0 on padding rows;
  *                  written only when ep_layout got topk_w
- *   err_flags[1]   EP_ERRFLAG_* bits raised by this layout */
+ *   err_flags[1]   EP_ERRFLAG_* bits raised by this layout
+ *   topk_idx       the caller's topk_idx the layout was built from (not a
+ *                  copy: the README's decode example returns
+ *                  cached_handle.topk_idx in place of a new recv_topk_idx,
+ *                  "Example use in inference decoding"); valid while the
+ *                  caller keeps that buffer, NULL for an empty batch */
 typedef struct {
     ep_config cfg;
     int32_t num_tokens;
@@ -143,6 +158,7 @@ typedef struct {
     float* row_w;
     uint32_t* err_flags;
     void* internal; /* workspace scratch for the layout kernels */
+    const void* topk_idx;
 } ep_handle;
 
 /* Bytes of workspace one layout needs (the README's get_buffer_size_hint).
@@ -150,7 +166,11 @@ typedef struct {
 size_t ep_workspace_bytes(const ep_config* cfg);
 
 /* Rows a receive buffer must have to hold any layout of this config without
- * knowing the counts: max_tokens*k + E*(A-1) (COMPACT) or E*C (FIXED).
+ * knowing the counts: max_tokens*k + E*(A-1) (COMPACT) or E*C (FIXED). The
+ * README sizes its buffer from num_max_tokens_per_rank and hidden before any
+ * routing is known (section "Interfaces and examples", "Buffer
+ * initialization": get_buffer_size_hint); this is the same bound for the
+ * receive rows, so a caller allocates them once and never waits for counts.
  * Returns -1 when the config is invalid. */
 int64_t ep_recv_rows_bound(const ep_config* cfg);
 
@@ -287,14 +307,19 @@ ep_status ep_handle_read_counts(const ep_handle* h, int32_t* cnt, int32_t* pad, 
                                 void* stream);
 
 /* Reads the handle's error word (EP_ERRFLAG_* bits) to host *flags.
- * Synchronises the stream. */
+ * Synchronises the stream. No passage of the pages defines this call: their
+ * API has no device-side data errors; it reports the two this library
+ * defines (an out-of-range expert id, a fixed-capacity overflow). */
 ep_status ep_handle_check(const ep_handle* h, uint32_t* flags, void* stream);
 
 /* Static text for a status code (an ep_status value; any other value
- * gives "EP_ERR_UNKNOWN"). */
+ * gives "EP_ERR_UNKNOWN"). No passage of the pages defines this call: it
+ * belongs to this C ABI's error convention. */
 const char* ep_status_string(int32_t s);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none). No passage
+ * of the pages defines this call: it belongs to this C ABI's error
+ * convention (the pages' Python API raises exceptions instead). */
 const char* ep_last_error_message(void);
 
 #ifdef __cplusplus

@@ -133,9 +133,34 @@ def test_status_strings():
 
 
 def test_struct_sizes_match_header():
-    # ep_config: 10 x 4 bytes; ep_handle: config + 2 ints + 10 pointers
+    # ep_config: 10 x 4 bytes; ep_handle: config + 2 ints + 11 pointers
     assert ctypes.sizeof(F.ep_config) == 40
-    assert ctypes.sizeof(F.ep_handle) == 40 + 8 + 10 * 8
+    assert ctypes.sizeof(F.ep_handle) == 40 + 8 + 11 * 8
+
+
+def test_struct_layout_matches_c_compiler(tmp_path):
+    """Every field offset and the size of the ctypes structs equal what a C
+    compiler gives for include/ep.h."""
+    import subprocess
+    lines = []
+    for st in (F.ep_config, F.ep_handle):
+        name = st.__name__
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (name, name))
+        for f, _ in st._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (name, f, name, f))
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "ep.h"\nint main(void) {\n%s\nreturn 0;\n}\n'
+                   % "\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {k: int(v) for k, v in (line.split() for line in out if line)}
+    for st in (F.ep_config, F.ep_handle):
+        name = st.__name__
+        assert got[name] == ctypes.sizeof(st), name
+        for f, _ in st._fields_:
+            assert got[name + "." + f] == getattr(st, f).offset, (name, f)
 
 
 def test_dispatch_forward_argument_errors():

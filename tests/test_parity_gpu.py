@@ -203,7 +203,7 @@ def test_every_tiny_fixed_table_single_launch():
 
 
 @pytest.mark.parametrize("T,H,E,k,A,D,dispatch", [
-    (64, 16384, 1024, 32, 2, 8, "fp8"),     # largest top-k and E; FP8 rows wider than 1024 lanes x 16 values
+    (64, 16384, 1024, 32, 2, 8, "fp8"),     # largest top-k and E; FP8 rows of exactly 1024 lanes x 16 values
     (40, 8200, 96, 32, 1, 4, "bf16"),       # 1025 vectors per row: every loop over a row wraps; 8200 % 128 != 0
     (33, 8, 40, 32, 3, 5, "bf16"),          # one vector per row, k = 32 of 40 experts
     (600, 8200, 64, 4, 8, 4, "bf16"),       # >= 512 tokens: combine rows in 9 pieces of 114 vectors, the last 113
