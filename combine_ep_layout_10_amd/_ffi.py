@@ -80,6 +80,9 @@ _SIGNATURES = {
                                  ctypes.POINTER(ep_handle), _P]),
     "ep_dispatch_forward": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
                                            ctypes.c_int32, _P, _P, _P, _P, ctypes.POINTER(ep_handle), _P]),
+    "ep_dispatch_forward_static_scratch": (ctypes.c_int, [ctypes.POINTER(ep_config), ctypes.c_int32, _P, _P, _P,
+                                                          ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P,
+                                                          ctypes.POINTER(ep_handle), _P]),
     "ep_dispatch": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P]),
     "ep_combine": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),

@@ -193,9 +193,32 @@ ep_status do_combine(const ep_handle* h, const void* y, const float* w, void* ou
     return EP_OK;
 }
 
+// Bytes of the multi-block layout's per-block partials for one call
+// (counts [nblk][E], distinct tokens [nblk][D], error bits [nblk]; regions
+// 256-byte aligned), and their offsets from the start of that scratch.
+struct PartMap {
+    size_t bpart, dpart, fpart, total;
+};
+
+PartMap part_map(const ep_config& c, int64_t pairs) {
+    int64_t nblk = (pairs + ep::kLayoutPairsPerBlock - 1) / ep::kLayoutPairsPerBlock;
+    if (nblk < 1) nblk = 1;
+    PartMap p;
+    p.bpart = 0;
+    p.dpart = round_up(4 * (size_t)c.num_experts * nblk, 256);
+    p.fpart = p.dpart + round_up(4 * (size_t)c.num_dests * nblk, 256);
+    p.total = p.fpart + round_up(4 * (size_t)nblk, 256);
+    return p;
+}
+
 // Checks a layout, builds its handle and kernel arguments; enqueues nothing.
+// scratch == nullptr: the per-block partials live in the workspace (which
+// must hold ep_workspace_bytes); otherwise they live at `scratch` (checked
+// by the caller to hold part_map(...).total bytes) and the workspace needs
+// only the handle's arrays.
 ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
-                         void* workspace, size_t workspace_bytes, ep_handle* out, ep::LayoutArgs* args, bool* small_out) {
+                         void* workspace, size_t workspace_bytes, ep_handle* out, ep::LayoutArgs* args, bool* small_out,
+                         char* scratch = nullptr) {
     ep_status s = check_config(cfg);
     if (s != EP_OK) return s;
     if (num_tokens < 0 || num_tokens > cfg->max_tokens)
@@ -206,8 +229,9 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
     const WsMap m = ws_map(*cfg);
     if (workspace == nullptr || !aligned(workspace, 256))
         return fail(EP_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
-    if (workspace_bytes < m.total)
-        return fail(EP_ERR_WORKSPACE, "workspace has %zu bytes, the config needs %zu", workspace_bytes, m.total);
+    const size_t need = scratch ? m.bpart : m.total;
+    if (workspace_bytes < need)
+        return fail(EP_ERR_WORKSPACE, "workspace has %zu bytes, the config needs %zu", workspace_bytes, need);
     char* ws = (char*)workspace;
     ep_handle h;
     memset(&h, 0, sizeof h);
@@ -222,7 +246,7 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
     h.slot = (int32_t*)(ws + m.slot);
     h.row_src = (int32_t*)(ws + m.rsrc);
     h.row_w = (float*)(ws + m.rw);
-    h.internal = ws + m.bpart;
+    h.internal = scratch ? (void*)scratch : (void*)(ws + m.bpart);
     h.topk_idx = num_tokens > 0 ? topk_idx : nullptr;
 
     const int64_t P = (int64_t)num_tokens * cfg->num_topk;
@@ -256,10 +280,78 @@ ep_status prepare_layout(const ep_config* cfg, int32_t num_tokens, const void* t
     a.row_src = h.row_src;
     a.row_w = h.row_w;
     a.err_flags = h.err_flags;
-    a.bpart = (int32_t*)(ws + m.bpart);
-    a.dpart = (int32_t*)(ws + m.dpart);
-    a.fpart = (uint32_t*)(ws + m.fpart);
+    if (scratch) {
+        const PartMap pm = part_map(*cfg, (int64_t)num_tokens * cfg->num_topk);
+        a.bpart = (int32_t*)(scratch + pm.bpart);
+        a.dpart = (int32_t*)(scratch + pm.dpart);
+        a.fpart = (uint32_t*)(scratch + pm.fpart);
+    } else {
+        a.bpart = (int32_t*)(ws + m.bpart);
+        a.dpart = (int32_t*)(ws + m.dpart);
+        a.fpart = (uint32_t*)(ws + m.fpart);
+    }
     *small_out = small;
+    *out = h;
+    return EP_OK;
+}
+
+// The multi-block layout's per-block partials for
+// ep_dispatch_forward_static_scratch: a library-held device array instead
+// of the caller's workspace, for callers that cannot allocate. Every entry a
+// call reads is written earlier in the same call (each layout block writes
+// its own counts, distinct-token counts and error bits before any block
+// reads them), so nothing needs clearing between calls.
+constexpr size_t kStaticScratchBytes = 1u << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with hipGetSymbolAddress (host code must never pass the array's
+// name itself to a kernel: on the host it is only a stand-in).
+ep_status static_scratch_address(char** out) {
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(EP_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = (char*)p;
+    return EP_OK;
+}
+
+// ep_dispatch_forward, with the layout's partials in `scratch` when given.
+ep_status dispatch_forward_impl(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
+                                void* workspace, size_t workspace_bytes, int32_t dtype, const void* x,
+                                const float* x_scales, void* recv, float* recv_scales, ep_handle* out, void* stream,
+                                char* scratch) {
+    ep_handle h;
+    ep::LayoutArgs la;
+    bool small = false;
+    ep_status s = check_config(cfg);
+    if (s != EP_OK) return s;
+    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out handle is NULL");
+    s = prepare_layout(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, &h, &la, &small, scratch);
+    if (s != EP_OK) return s;
+    ep::DispatchArgs da;
+    int kind = 0;
+    s = prepare_dispatch(&h, dtype, x, x_scales, nullptr, recv, recv_scales, &da, &kind);
+    if (s != EP_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (small && ep::fused_layout_dispatch_fits((int64_t)num_tokens * cfg->num_topk, cfg->num_experts)) {
+        e = ep::launch_layout_dispatch_small(kind, la, da, st);
+        if (e != hipSuccess) return hip_fail(e, "layout + dispatch launch");
+    } else {
+        e = ep::launch_layout(la, small, st);
+        if (e != hipSuccess) return hip_fail(e, "layout launch");
+        e = ep::launch_dispatch(kind, da, st);
+        if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+    }
     *out = h;
     return EP_OK;
 }
@@ -347,31 +439,29 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
 ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const void* topk_idx, const float* topk_w,
                               void* workspace, size_t workspace_bytes, int32_t dtype, const void* x,
                               const float* x_scales, void* recv, float* recv_scales, ep_handle* out, void* stream) {
-    ep_handle h;
-    ep::LayoutArgs la;
-    bool small = false;
+    return dispatch_forward_impl(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, dtype, x, x_scales,
+                                 recv, recv_scales, out, stream, nullptr);
+}
+
+ep_status ep_dispatch_forward_static_scratch(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
+                                             const float* topk_w, void* workspace, size_t workspace_bytes,
+                                             int32_t dtype, const void* x, const float* x_scales, void* recv,
+                                             float* recv_scales, ep_handle* out, void* stream) {
     ep_status s = check_config(cfg);
     if (s != EP_OK) return s;
-    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out handle is NULL");
-    s = prepare_layout(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, &h, &la, &small);
+    if (num_tokens < 0 || num_tokens > cfg->max_tokens)
+        return fail(EP_ERR_INVALID_ARG, "num_tokens %d outside [0, %d]", num_tokens, cfg->max_tokens);
+    const PartMap pm = part_map(*cfg, (int64_t)num_tokens * cfg->num_topk);
+    if (pm.total > kStaticScratchBytes)
+        return fail(EP_ERR_WORKSPACE,
+                    "the layout's per-block partials need %zu bytes, more than the library's %zu-byte static scratch "
+                    "(ep_dispatch_forward takes them from the workspace instead)",
+                    pm.total, (size_t)kStaticScratchBytes);
+    char* scr = nullptr;
+    s = static_scratch_address(&scr);
     if (s != EP_OK) return s;
-    ep::DispatchArgs da;
-    int kind = 0;
-    s = prepare_dispatch(&h, dtype, x, x_scales, nullptr, recv, recv_scales, &da, &kind);
-    if (s != EP_OK) return s;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e;
-    if (small && ep::fused_layout_dispatch_fits((int64_t)num_tokens * cfg->num_topk, cfg->num_experts)) {
-        e = ep::launch_layout_dispatch_small(kind, la, da, st);
-        if (e != hipSuccess) return hip_fail(e, "layout + dispatch launch");
-    } else {
-        e = ep::launch_layout(la, small, st);
-        if (e != hipSuccess) return hip_fail(e, "layout launch");
-        e = ep::launch_dispatch(kind, da, st);
-        if (e != hipSuccess) return hip_fail(e, "dispatch launch");
-    }
-    *out = h;
-    return EP_OK;
+    return dispatch_forward_impl(cfg, num_tokens, topk_idx, topk_w, workspace, workspace_bytes, dtype, x, x_scales,
+                                 recv, recv_scales, out, stream, scr);
 }
 
 ep_status ep_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales, void* recv,

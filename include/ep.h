@@ -207,6 +207,28 @@ ep_status ep_dispatch_forward(const ep_config* cfg, int32_t num_tokens, const vo
                               int32_t dtype, const void* x, const float* x_scales, void* recv,
                               float* recv_scales, ep_handle* out, void* stream);
 
+/* ep_dispatch_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, checks and results (bit-identical handle,
+ * recv and recv_scales), except where the multi-block layout keeps its
+ * per-block partials (counts [nblk, E], distinct tokens [nblk, D], error
+ * bits [nblk]; nblk = ceil(num_tokens * k / 1024), each region rounded up
+ * to 256 bytes): in a static device array the library holds (1 MiB per
+ * GPU, kept until the process ends) instead of the workspace. The
+ * workspace then needs only the handle's arrays; ep_workspace_bytes(cfg)
+ * always suffices. Allocates nothing, on the host or the device. The first
+ * call on each device looks up the array's address (hipGetSymbolAddress,
+ * not a stream operation). A layout whose partials exceed 1 MiB returns
+ * EP_ERR_WORKSPACE and enqueues nothing. Every call on one GPU shares the
+ * array: calls whose work overlaps on one GPU (concurrent streams) race and
+ * must be ordered by the caller; consecutive calls on one stream are safe,
+ * since every entry a call reads is written earlier in that call. Small
+ * batches (the single launch) use no partials. */
+ep_status ep_dispatch_forward_static_scratch(const ep_config* cfg, int32_t num_tokens, const void* topk_idx,
+                                             const float* topk_w, void* workspace, size_t workspace_bytes,
+                                             int32_t dtype, const void* x, const float* x_scales, void* recv,
+                                             float* recv_scales, ep_handle* out, void* stream);
+
 /* Dispatch on an existing handle (README dispatch_forward, or dispatch with a
  * cached handle: no layout work, no synchronisation).
  *   x          device [T, hidden]: bf16 (EP_BF16, EP_FP8_QUANTIZE) or E4M3FN

@@ -217,3 +217,24 @@ def test_grouped_gemm_argument_errors():
     assert g(ctypes.byref(h), fake, fake, fake, fake, 256, None, None) == F.EP_ERR_INVALID_ARG
     assert g(ctypes.byref(h), fake, fake, fake, fake, 256, odd, None) == F.EP_ERR_INVALID_ARG
     assert "16-byte" in F.last_error_message()
+
+
+def test_static_scratch_rejects_layouts_beyond_its_array():
+    """ep_dispatch_forward_static_scratch: a layout whose per-block partials
+    exceed the 1 MiB static array is refused before any device work (the
+    check precedes the array's lookup, so it runs without a GPU)."""
+    lib = F.lib()
+    # 1024 experts, 1024 destinations, 2^20 pairs: 1024 blocks x (1024 + 1024 + 1) ints
+    c = cfg(max_tokens=1 << 17, hidden=128, num_experts=1024, num_topk=8, num_dests=1024, expert_alignment=1)
+    h = F.ep_handle()
+    st = lib.ep_dispatch_forward_static_scratch(ctypes.byref(c), 1 << 17, None, None, None, 0, F.EP_BF16, None,
+                                                None, None, None, ctypes.byref(h), None)
+    assert st == F.EP_ERR_WORKSPACE
+    assert "static scratch" in F.last_error_message()
+    # invalid configs and token counts are rejected as by ep_dispatch_forward
+    bad = cfg(num_experts=0)
+    assert lib.ep_dispatch_forward_static_scratch(ctypes.byref(bad), 1, None, None, None, 0, F.EP_BF16, None,
+                                                  None, None, None, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
+    c = cfg()
+    assert lib.ep_dispatch_forward_static_scratch(ctypes.byref(c), 65, None, None, None, 0, F.EP_BF16, None,
+                                                  None, None, None, ctypes.byref(h), None) == F.EP_ERR_INVALID_ARG
