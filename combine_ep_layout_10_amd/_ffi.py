@@ -147,9 +147,11 @@ def ep_dispatch_forward(cfg: ep_config, num_tokens: int, topk_idx: int, topk_w, 
                         workspace_bytes: int, dtype: int, x: int, x_scales, recv: int, recv_scales,
                         stream: int) -> ep_handle:
     h = ep_handle()
-    _check(lib().ep_dispatch_forward(ctypes.byref(cfg), int(num_tokens), topk_idx, topk_w, workspace,
-                                     int(workspace_bytes), int(dtype), x, x_scales, recv, recv_scales,
-                                     ctypes.byref(h), stream), "ep_dispatch_forward")
+    st = (_lib or lib()).ep_dispatch_forward(ctypes.byref(cfg), num_tokens, topk_idx, topk_w, workspace,
+                                             workspace_bytes, dtype, x, x_scales, recv, recv_scales,
+                                             ctypes.byref(h), stream)
+    if st != EP_OK:
+        _check(st, "ep_dispatch_forward")
     return h
 
 
@@ -158,7 +160,9 @@ def ep_dispatch(h: ep_handle, dtype: int, x: int, x_scales, recv: int, recv_scal
 
 
 def ep_combine(h: ep_handle, y: int, topk_w, out: int, row_vals, out_vals, stream: int) -> None:
-    _check(lib().ep_combine(ctypes.byref(h), y, topk_w, out, row_vals, out_vals, stream), "ep_combine")
+    st = (_lib or lib()).ep_combine(ctypes.byref(h), y, topk_w, out, row_vals, out_vals, stream)
+    if st != EP_OK:
+        _check(st, "ep_combine")
 
 
 def ep_dispatch_backward(h: ep_handle, grad_recv: int, grad_row_w, grad_x: int, grad_topk_w, stream: int) -> None:

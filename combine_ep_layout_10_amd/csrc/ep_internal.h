@@ -157,8 +157,77 @@ hipError_t launch_dispatch(int kind, const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_weight_grad(const WeightGradArgs& a, hipStream_t stream);
 hipError_t launch_grouped_gemm_fp8(const GemmArgs& a, int64_t rows_bound, hipStream_t stream);
+// Kernel arguments of the single-launch layout + dispatch, packed into the
+// fields that kernel reads: the handle's arrays as 32-bit offsets from the
+// workspace base, small sizes as 16-bit fields. A launch costs the host
+// about 3 ns per byte of kernel arguments on this part (measured: 3.84 us
+// for 320 bytes, 2.96 us for 12), and this launch sits on the decode path.
+struct FusedArgs {
+    const void* idx;
+    const float* w;
+    char* ws;  // the handle's arrays live at ws + o_*
+    const void* x;
+    const float* x_scales;
+    void* recv;
+    float* recv_scales;
+    uint32_t o_cnt, o_pad, o_eoff, o_doff, o_dtok, o_slot, o_rsrc, o_rw, o_flags;
+    int32_t T, H, A, C, pad_pieces_per_expert, npad_blocks;
+    int16_t E, k, D, epd, nbits, idx_bits, mode, zero_pad, nsplit, seg, pad_rows_per_piece;
+};
+
+__host__ __device__ inline LayoutArgs fused_layout_args(const FusedArgs& f) {
+    LayoutArgs a = {};
+    a.idx = f.idx;
+    a.w = f.w;
+    a.idx_bits = f.idx_bits;
+    a.T = f.T;
+    a.E = f.E;
+    a.k = f.k;
+    a.A = f.A;
+    a.D = f.D;
+    a.C = f.C;
+    a.mode = f.mode;
+    a.nbits = f.nbits;
+    a.epd = f.epd;
+    a.cnt = (int32_t*)(f.ws + f.o_cnt);
+    a.pad = (int32_t*)(f.ws + f.o_pad);
+    a.expert_off = (int32_t*)(f.ws + f.o_eoff);
+    a.dest_off = (int32_t*)(f.ws + f.o_doff);
+    a.dest_tokens = (int32_t*)(f.ws + f.o_dtok);
+    a.slot = (int32_t*)(f.ws + f.o_slot);
+    a.row_src = (int32_t*)(f.ws + f.o_rsrc);
+    a.row_w = (float*)(f.ws + f.o_rw);
+    a.err_flags = (uint32_t*)(f.ws + f.o_flags);
+    return a;
+}
+
+__host__ __device__ inline DispatchArgs fused_dispatch_args(const FusedArgs& f) {
+    DispatchArgs d = {};
+    d.x = f.x;
+    d.x_scales = f.x_scales;
+    d.recv = f.recv;
+    d.recv_scales = f.recv_scales;
+    d.slot = (const int32_t*)(f.ws + f.o_slot);
+    d.cnt = (const int32_t*)(f.ws + f.o_cnt);
+    d.pad = (const int32_t*)(f.ws + f.o_pad);
+    d.expert_off = (const int32_t*)(f.ws + f.o_eoff);
+    d.T = f.T;
+    d.H = f.H;
+    d.k = f.k;
+    d.E = f.E;
+    d.zero_pad = f.zero_pad;
+    d.pad_rows_per_piece = f.pad_rows_per_piece;
+    d.pad_pieces_per_expert = f.pad_pieces_per_expert;
+    d.npad_blocks = f.npad_blocks;
+    d.nsplit = f.nsplit;
+    d.seg = f.seg;
+    return d;
+}
+
 // Single-launch layout + dispatch (unweighted kinds) for small batches.
 bool fused_layout_dispatch_fits(int64_t pairs, int E);
-hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, hipStream_t stream);
+// ws: the workspace base that every handle array of `la` lies in.
+hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, char* ws,
+                                        hipStream_t stream);
 
 }  // namespace ep

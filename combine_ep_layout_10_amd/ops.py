@@ -45,8 +45,13 @@ class Config:
     flags: int = 0
 
     def c(self) -> F.ep_config:
-        return F.ep_config(self.max_tokens, self.hidden, self.num_experts, self.num_topk, self.num_dests,
-                           self.expert_alignment, self.capacity, self.mode, self.idx_bits, self.flags)
+        """The C struct, built once per Config (cached on the instance)."""
+        c = self.__dict__.get("_c_struct")
+        if c is None:
+            c = F.ep_config(self.max_tokens, self.hidden, self.num_experts, self.num_topk, self.num_dests,
+                            self.expert_alignment, self.capacity, self.mode, self.idx_bits, self.flags)
+            object.__setattr__(self, "_c_struct", c)
+        return c
 
     def workspace_bytes(self) -> int:
         n = F.ep_workspace_bytes(self.c())
@@ -55,44 +60,60 @@ class Config:
         return n
 
     def recv_rows_bound(self) -> int:
-        n = _ROWS_BOUND.get(self)
+        n = self.__dict__.get("_rows_bound")
         if n is None:
             n = F.ep_recv_rows_bound(self.c())
             if n < 0:
                 raise F.EPError(F.EP_ERR_INVALID_ARG, "ep_recv_rows_bound", F.last_error_message())
-            _ROWS_BOUND[self] = n
+            object.__setattr__(self, "_rows_bound", n)
         return n
 
 
-_ROWS_BOUND = {}
+_current_device = torch.cuda.current_device
+_raw_stream = torch._C._cuda_getCurrentRawStream
 
 
-def _stream() -> int:
-    return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
+def _stream(cur: Optional[int] = None) -> int:
+    return _raw_stream(_current_device() if cur is None else cur)
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+def _bad_tensor(t, name: str, dtype, cur: int) -> ValueError:
+    """The error for a tensor _dev refused (built only on failure)."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % name)
-    if t.device.index != torch.cuda.current_device():
+        return ValueError("%s must be a device tensor" % name)
+    if t.get_device() != cur:
         # kernels run on the current device's stream
-        raise ValueError("%s is on %s, not on the current device cuda:%d" % (name, t.device, torch.cuda.current_device()))
+        return ValueError("%s is on %s, not on the current device cuda:%d" % (name, t.device, cur))
     if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
-        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+        return ValueError("%s must be contiguous" % name)
+    return ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, cur: Optional[int] = None) -> int:
+    """Device pointer of a contiguous tensor on the current device (cur: that
+    device's index, when the caller already has it), of the given dtype (one
+    dtype, or a tuple of them; torch dtypes are singletons, so identity
+    decides)."""
+    if cur is None:
+        cur = _current_device()
+    try:
+        dt = t.dtype
+        ok = (dtype is None or dt is dtype or (type(dtype) is tuple and dt in dtype)) and \
+            t.get_device() == cur and t.is_contiguous()
+    except AttributeError:
+        ok = False
+    if not ok:
+        raise _bad_tensor(t, name, dtype, cur)
     return t.data_ptr()
 
 
-def _opt(t: Optional[torch.Tensor], name: str, dtype=None):
-    return None if t is None else _dev(t, name, dtype)
+def _opt(t: Optional[torch.Tensor], name: str, dtype=None, cur: Optional[int] = None):
+    return None if t is None else _dev(t, name, dtype, cur)
 
 
 def _need(t: Optional[torch.Tensor], shape, name: str) -> None:
     """The kernels index these buffers by the handle's sizes: check them here."""
-    if t is None:
-        return
-    if tuple(t.shape) != tuple(shape):
+    if t is not None and t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
@@ -100,6 +121,8 @@ class Handle:
     """An ep_handle plus the workspace tensor it points into and the topk_idx
     tensor the layout was built from (README "Example use in inference
     decoding": a cached handle hands back its topk_idx)."""
+
+    __slots__ = ("cfg", "c", "workspace", "_topk_idx")
 
     def __init__(self, cfg: Config, h: F.ep_handle, workspace: torch.Tensor,
                  topk_idx: Optional[torch.Tensor] = None):
@@ -173,14 +196,8 @@ class Handle:
         return F.ep_handle_check(self.c, _stream())
 
 
-_C_CONFIG = {}
-
-
 def _c_config(cfg: Config) -> F.ep_config:
-    c = _C_CONFIG.get(cfg)
-    if c is None:
-        c = _C_CONFIG[cfg] = cfg.c()
-    return c
+    return cfg.c()
 
 
 def new_workspace(cfg: Config, device="cuda") -> torch.Tensor:
@@ -237,11 +254,13 @@ def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype
                      recv_scales: Optional[torch.Tensor] = None):
     """Layout + dispatch in one call (README dispatch_forward). Returns
     (handle, recv) or (handle, recv, recv_scales) for the FP8 types."""
+    cur = _current_device()
     idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
-    T, H, R = int(topk_idx.shape[0]), cfg.hidden, cfg.recv_rows_bound()
-    if topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+    shape = topk_idx.shape
+    if len(shape) != 2 or shape[1] != cfg.num_topk:
         raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
-    if topk_w is not None and tuple(topk_w.shape) != tuple(topk_idx.shape):
+    T, H, R = shape[0], cfg.hidden, cfg.recv_rows_bound()
+    if topk_w is not None and topk_w.shape != shape:
         raise ValueError("topk_w must match topk_idx")
     _need(x, (T, H), "x")
     if dtype == FP8_PREQUANT:
@@ -257,11 +276,12 @@ def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype
     if fp8:
         _need(recv_scales, (R, H // 128), "recv_scales")
     xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
-    c = F.ep_dispatch_forward(_c_config(cfg), T, _dev(topk_idx, "topk_idx", idx_dtype),
-                              _opt(topk_w, "topk_w", torch.float32), _dev(workspace, "workspace", torch.uint8),
-                              workspace.numel(), dtype, _dev(x, "x", xdt), _opt(x_scales, "x_scales", torch.float32),
-                              _dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16),
-                              _opt(recv_scales, "recv_scales", torch.float32), _stream())
+    c = F.ep_dispatch_forward(cfg.c(), T, _dev(topk_idx, "topk_idx", idx_dtype, cur),
+                              _opt(topk_w, "topk_w", torch.float32, cur),
+                              _dev(workspace, "workspace", torch.uint8, cur), workspace.numel(), dtype,
+                              _dev(x, "x", xdt, cur), _opt(x_scales, "x_scales", torch.float32, cur),
+                              _dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16, cur),
+                              _opt(recv_scales, "recv_scales", torch.float32, cur), _raw_stream(cur))
     h = Handle(cfg, c, workspace, topk_idx)
     return (h, recv, recv_scales) if fp8 else (h, recv)
 
@@ -269,17 +289,19 @@ def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype
 def combine(h: Handle, y: torch.Tensor, topk_w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             row_vals: Optional[torch.Tensor] = None):
     """Returns out [T, H] bf16 (and out_vals [T, k] when row_vals is given)."""
-    T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
-    _need(y, (h.cfg.recv_rows_bound(), H), "y")
+    cur = _current_device()
+    cfg = h.cfg
+    T, H, k, R = h.c.num_tokens, cfg.hidden, cfg.num_topk, cfg.recv_rows_bound()
+    _need(y, (R, H), "y")
     _need(topk_w, (T, k), "topk_w")
-    _need(row_vals, (h.cfg.recv_rows_bound(),), "row_vals")
+    _need(row_vals, (R,), "row_vals")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _need(out, (T, H), "out")
     out_vals = None if row_vals is None else torch.empty((T, k), dtype=torch.float32, device=y.device)
-    F.ep_combine(h.c, _dev(y, "y", torch.bfloat16), _opt(topk_w, "topk_w", torch.float32),
-                 _dev(out, "out", torch.bfloat16), _opt(row_vals, "row_vals", torch.float32),
-                 _opt(out_vals, "out_vals", torch.float32), _stream())
+    F.ep_combine(h.c, _dev(y, "y", torch.bfloat16, cur), _opt(topk_w, "topk_w", torch.float32, cur),
+                 _dev(out, "out", torch.bfloat16, cur), _opt(row_vals, "row_vals", torch.float32, cur),
+                 _opt(out_vals, "out_vals", torch.float32, cur), _raw_stream(cur))
     return out if row_vals is None else (out, out_vals)
 
 
