@@ -263,13 +263,14 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 // wave-uniform base (scalar register pair) plus a 32-bit per-lane byte
 // offset, so that the per-lane part stays fixed over the K loop; `lds` is the
 // wave's LDS destination (uniform), lane i's data lands at lds + size * i.
+// The LDS address goes in through an m0 input operand: the compiler writes
+// m0 itself and knows what it holds (the asm never writes it); the s_nop is
+// the one wait state an m0 write needs before an LDS DMA reads it.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
