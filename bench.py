@@ -73,6 +73,9 @@ def parse():
                    help="copies of x and grad_out the eager steps cycle through (each step reads inputs no cache "
                         "holds: 4 copies of x and grad_out are 0.94 GB at the V3 shape, against a 256 MB MALL); "
                         "1 = the same inputs every step")
+    p.add_argument("--no-warm", action="store_true",
+                   help="skip the reference pass on one unrotated copy of the inputs (so that every call of the "
+                        "run reads rotated inputs, as a profiled run should)")
     p.add_argument("--no-flush", action="store_true",
                    help="skip the per-kernel pass with L2 and MALL flushed before each kernel")
     p.add_argument("--no-copy-ceiling", action="store_true",
@@ -390,7 +393,7 @@ def main():
     k_ms = {n: float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in evs])) for i, n in enumerate(names)}
     gpu_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
     warm = None
-    if nrot > 1:
+    if nrot > 1 and not args.no_warm:
         # the same calls on the same inputs every step (x and grad_out stay
         # in the MALL between steps): for reference only
         wev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 2)] for _ in range(args.steps)]
@@ -579,13 +582,18 @@ def bench_call(args):
     gen = torch.Generator(device=dev)
     gen.manual_seed(6)
     grad_out = torch.randn((wl.T, wl.H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    # grad_out (read with plain loads) cycles through copies, as in the path's
+    # steps, so each call reads it from HBM
+    nrot = max(1, args.rotate)
+    gos = [grad_out] + [grad_out.clone() for _ in range(nrot - 1)]
+    cur = [0]
     T, H, k = wl.T, wl.H, wl.k
     if args.step == "weight_grad":
         y = torch.randn((R_cap, H), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
         gw = torch.empty((T, k), dtype=torch.float32, device=dev)
 
         def call():
-            ops.combine_weight_grad(h, grad_out, y, gw)
+            ops.combine_weight_grad(h, gos[cur[0] % nrot], y, gw)
         # grad_out and the pairs' rows of y in, slots in, one float per pair out
         nbytes = T * H * 2 + P * H * 2 + T * k * 4 + T * k * 4
         kname, what = "k_weight_grad", "ep_combine_weight_grad"
@@ -594,7 +602,7 @@ def bench_call(args):
         gs = torch.empty((R_cap, H // 128), dtype=torch.float32, device=dev)
 
         def call():
-            ops.combine_backward(h, grad_out, ops.FP8_QUANTIZE, w, grad_y=gq, grad_y_scales=gs)
+            ops.combine_backward(h, gos[cur[0] % nrot], ops.FP8_QUANTIZE, w, grad_y=gq, grad_y_scales=gs)
         # grad_out, slots and weights in; every row (pairs and zero padding)
         # with its 1x128 scales out
         nbytes = T * H * 2 + T * k * 4 + T * k * 4 + R * (H + 4 * (H // 128))
@@ -602,12 +610,14 @@ def bench_call(args):
     stream = torch.cuda.current_stream()
     if args.calib_copy:
         calib_copy(dev)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        cur[0] = i
         call()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for i, (e0, e1) in enumerate(ev):
+        cur[0] = args.warmup + i
         e0.record(stream)
         call()
         e1.record(stream)
@@ -640,7 +650,8 @@ def bench_call(args):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic(kname, khash, wl.name + "_" + args.step),
                      "kernel": kname, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": round(launch_ms * 1e3, 2), "timed": "events in the timed region"},
+                     "avg_launch_us": round(launch_ms * 1e3, 2), "timed": "events in the timed region",
+                     "inputs": "grad_out cycled through %d copies" % nrot},
         "cpu_baseline": cpu,
         "kernels": {"kernel_bytes": {kname: nbytes}, "kernel_hash": khash, "pairs": P, "rows": R},
     }

@@ -346,7 +346,12 @@ ep_status dispatch_forward_impl(const ep_config* cfg, int32_t num_tokens, const 
     // the single launch addresses the handle's arrays by 32-bit offsets
     // from the workspace base
     const bool offsets32 = ws_map(*cfg).bpart <= 0xFFFFFFFFull;
-    if (small && offsets32 && ep::fused_layout_dispatch_fits((int64_t)num_tokens * cfg->num_topk, cfg->num_experts)) {
+    bool fused = false;
+    if (small && offsets32) {
+        e = ep::fused_layout_dispatch_fits(la, da, &fused);
+        if (e != hipSuccess) return hip_fail(e, "device query");
+    }
+    if (fused) {
         e = ep::launch_layout_dispatch_small(kind, la, da, (char*)workspace, st);
         if (e != hipSuccess) return hip_fail(e, "layout + dispatch launch");
     } else {

@@ -289,7 +289,24 @@ static FusedArgs pack_fused(const LayoutArgs& la, const DispatchArgs& da, char* 
     return f;
 }
 
-bool fused_layout_dispatch_fits(int64_t pairs, int E) { return pairs <= kSmallMaxPairs && E <= kSmallMaxExperts; }
+hipError_t fused_layout_dispatch_fits(const LayoutArgs& la, const DispatchArgs& da, bool* fits) {
+    *fits = false;
+    if ((int64_t)la.T * la.k > kSmallMaxPairs || la.E > kSmallMaxExperts) return hipSuccess;
+    // Each zero-fill piece of the single launch takes a block that redoes
+    // the small layout; once those blocks and one per token exceed the
+    // resident blocks, the grid runs in rounds and the two launches (layout,
+    // then the dispatch kernel's capped zero-fill loop) are faster.
+    DispatchArgs d = da;
+    set_pad_pieces(d, kFusedPadRowsPerPiece);
+    if (d.npad_blocks > 0) {
+        int cus = 0;
+        const hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if ((int64_t)la.T + d.npad_blocks > (int64_t)kFusedBlocksPerCU * cus) return hipSuccess;
+    }
+    *fits = true;
+    return hipSuccess;
+}
 
 hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& args, char* ws,
                                         hipStream_t stream) {

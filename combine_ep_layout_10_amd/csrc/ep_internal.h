@@ -225,7 +225,10 @@ __host__ __device__ inline DispatchArgs fused_dispatch_args(const FusedArgs& f) 
 }
 
 // Single-launch layout + dispatch (unweighted kinds) for small batches.
-bool fused_layout_dispatch_fits(int64_t pairs, int E);
+// Whether ep_dispatch_forward takes the single launch: pairs <= 4096,
+// E <= 512, and its zero-fill blocks plus one block per token fit the
+// resident blocks.
+hipError_t fused_layout_dispatch_fits(const LayoutArgs& la, const DispatchArgs& da, bool* fits);
 // ws: the workspace base that every handle array of `la` lies in.
 hipError_t launch_layout_dispatch_small(int kind, const LayoutArgs& la, const DispatchArgs& da, char* ws,
                                         hipStream_t stream);

@@ -197,7 +197,9 @@ ep_status ep_layout(const ep_config* cfg, int32_t num_tokens, const void* topk_i
  * checked before anything is enqueued. The results (handle contents, recv,
  * recv_scales) are bit-identical to ep_layout followed by ep_dispatch.
  * Small batches (num_tokens * k <= 4096 and E <= 512, the decode sizes of
- * README "Example use in inference decoding") take a single kernel launch:
+ * README "Example use in inference decoding", whose zero-fill of padding
+ * rows, if any, fits the CUs beside one block per token) take a single
+ * kernel launch:
  * every block derives its rows from all the batch's ids (the whole small
  * layout in LDS, or, in FIXED mode and with expert_alignment 1, only the
  * counts that place its own pairs), so no block waits on another. Larger batches enqueue the layout kernels and then the dispatch

@@ -81,6 +81,19 @@ def test_traffic_scaling_and_recorded_kernels(tmp_path):
     assert "ep::k_layout_count" in md and "| 7000000 |" in md
 
 
+def test_copy_scale_ignores_smaller_copies_on_the_same_grid(tmp_path):
+    """The benchmark's copies of its inputs run as copyBuffer dispatches with
+    the same grid as the 1 GiB calibration copy; only the largest counter
+    values (the 1 GiB copies) set the scale."""
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = (1 << 30) / 1024
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 131072, 114688.0)] * 6 +
+                 [(copy, 512, 1.0), (copy, 131072, gib_kib), (copy, 131072, gib_kib * 1.001)])
+    scale, kib = ps.copy_scale(ps.read_counter(str(tmp_path / "w.csv"), "WRITE_SIZE"))
+    assert abs(kib - gib_kib * 1.0005) < 1e-6 * gib_kib
+    assert abs(scale - 1 / 1.0005) < 1e-9
+
+
 def test_traffic_needs_the_copy(tmp_path):
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [("void ep::k_combine<true>(ep::CombineArgs)", 1, 1.0)])
     with pytest.raises(SystemExit):

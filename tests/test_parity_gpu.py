@@ -294,6 +294,8 @@ def test_argument_errors_enqueue_nothing():
     (513, 512, 8, 8, 8, 0, 0, "bf16", 0.0, 0.0),         # P = 4104: layout + dispatch launches
     (300, 513, 2, 4, 3, 0, 0, "bf16", 0.0, 0.0),         # E = 513: layout + dispatch launches
     (1, 16, 4, 4, 2, 0, 0, "fp8", 0.0, 0.0),             # one token
+    (16, 256, 8, 128, 8, 0, 0, "fp8", 0.0, 0.0),         # 2,048 zero-fill pieces: layout + dispatch launches
+    (40, 64, 6, 128, 4, 0, 0, "bf16", 0.0, 0.0),         # 512 zero-fill pieces + 40 tokens: two launches
 ])
 def test_dispatch_forward(T, E, k, A, D, C, mode, dispatch, masked, bad):
     H = 7168 if (T, E) == (128, 256) else 256
