@@ -29,8 +29,33 @@ def command(out: str = LIB, extra=()) -> list:
     return [HIPCC] + FLAGS + list(extra) + ["-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
+TORCH_SRC = os.path.join(CSRC, "ep_torch.cpp")
+TORCH_EXT = os.path.join(HERE, "_ep_torch.so")
+
+
+def build_torch_binding(verbose: bool = False) -> str:
+    """Compile the torch binding (csrc/ep_torch.cpp, host C++ against the
+    installed torch headers) into _ep_torch.so beside libep.so, which it
+    links (rpath $ORIGIN)."""
+    import shutil
+    from torch.utils import cpp_extension
+    bdir = os.path.join(HERE, "_build", "torch_ext")
+    os.makedirs(bdir, exist_ok=True)
+    cpp_extension.load(name="_ep_torch", sources=[TORCH_SRC], build_directory=bdir, verbose=verbose,
+                       with_cuda=False, is_python_module=True, extra_cflags=["-O2"],
+                       # runpath $ORIGIN (the package, where the copy below lives) and
+                       # $ORIGIN/../.. (the package again, seen from the build folder, where
+                       # load() imports it once), escaped for ninja ($$) and the shell (\$)
+                       extra_ldflags=["-L" + HERE, "-lep", "-Wl,-rpath,\\$$ORIGIN:\\$$ORIGIN/../.."])
+    tmp = TORCH_EXT + ".tmp%d" % os.getpid()
+    shutil.copyfile(os.path.join(bdir, "_ep_torch.so"), tmp)
+    os.replace(tmp, TORCH_EXT)
+    return TORCH_EXT
+
+
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile every HIP source into libep.so (always recompiles)."""
+    """Compile every HIP source into libep.so, then the torch binding that
+    links it (always recompiles both)."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = command(tmp, extra)
     if verbose:
@@ -40,6 +65,7 @@ def build(verbose: bool = False, extra=()) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libep.so")
     os.replace(tmp, LIB)
+    build_torch_binding(verbose)
     return LIB
 
 

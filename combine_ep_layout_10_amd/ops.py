@@ -15,6 +15,7 @@ Mapping to the DeepEP README ("Interfaces and examples"):
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 from typing import Optional, Tuple
 
@@ -22,6 +23,27 @@ import numpy as np
 import torch
 
 from . import _ffi as F
+
+_TORCH_EXT = __import__("os").path.join(__import__("os").path.dirname(__file__), "_ep_torch.so")
+
+
+def _load_binding():
+    """The compiled binding (_ep_torch.so, built beside libep.so): the tensor
+    checks and the C calls of the hot entry points. Raises if it has not
+    been built; there is no other path."""
+    import importlib.util
+    import os
+    if not os.path.exists(_TORCH_EXT):
+        raise ImportError("_ep_torch.so not found at %s: build it with `python -m combine_ep_layout_10_amd.build`"
+                          % _TORCH_EXT)
+    F.lib()  # libep.so first, through ctypes: the binding links the same file
+    spec = importlib.util.spec_from_file_location(__package__ + "._ep_torch", _TORCH_EXT)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_B = _load_binding()
 
 MODE_COMPACT = F.EP_MODE_COMPACT
 MODE_FIXED = F.EP_MODE_FIXED
@@ -51,7 +73,16 @@ class Config:
             c = F.ep_config(self.max_tokens, self.hidden, self.num_experts, self.num_topk, self.num_dests,
                             self.expert_alignment, self.capacity, self.mode, self.idx_bits, self.flags)
             object.__setattr__(self, "_c_struct", c)
+            object.__setattr__(self, "_c_addr", ctypes.addressof(c))
         return c
+
+    def c_addr(self) -> int:
+        """Address of the cached C struct (the compiled binding reads it)."""
+        a = self.__dict__.get("_c_addr")
+        if a is None:
+            self.c()
+            a = self.__dict__["_c_addr"]
+        return a
 
     def workspace_bytes(self) -> int:
         n = F.ep_workspace_bytes(self.c())
@@ -206,16 +237,11 @@ def new_workspace(cfg: Config, device="cuda") -> torch.Tensor:
 
 def layout(cfg: Config, topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None) -> Handle:
-    idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
-    T = int(topk_idx.shape[0])
-    if topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
-        raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
-    if topk_w is not None and tuple(topk_w.shape) != tuple(topk_idx.shape):
-        raise ValueError("topk_w must match topk_idx")
+    cur = _current_device()
     if workspace is None:
         workspace = new_workspace(cfg, topk_idx.device)
-    h = F.ep_layout(_c_config(cfg), T, _dev(topk_idx, "topk_idx", idx_dtype), _opt(topk_w, "topk_w", torch.float32),
-                    _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+    h = F.ep_handle()
+    _B.layout(cfg.c_addr(), topk_idx, topk_w, workspace, ctypes.addressof(h), _raw_stream(cur), cur)
     return Handle(cfg, h, workspace, topk_idx)
 
 
@@ -232,19 +258,9 @@ def _recv_buffers(h: Handle, dtype: int, device, recv, recv_scales):
 def dispatch(h: Handle, x: torch.Tensor, dtype: int = BF16, x_scales: Optional[torch.Tensor] = None,
              recv: Optional[torch.Tensor] = None, recv_scales: Optional[torch.Tensor] = None):
     """Returns recv (and recv_scales for the FP8 types)."""
-    T, H, R = h.num_tokens, h.cfg.hidden, h.cfg.recv_rows_bound()
-    _need(x, (T, H), "x")
-    if dtype == FP8_PREQUANT:
-        _need(x_scales, (T, H // 128), "x_scales")
-    xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
+    cur = _current_device()
     recv, recv_scales = _recv_buffers(h, dtype, x.device, recv, recv_scales)
-    _need(recv, (R, H), "recv")
-    if dtype != BF16:
-        _need(recv_scales, (R, H // 128), "recv_scales")
-    F.ep_dispatch(h.c, dtype, _dev(x, "x", xdt), _opt(x_scales, "x_scales", torch.float32),
-                  _dev(recv, "recv", torch.uint8 if dtype != BF16 else torch.bfloat16),
-                  _opt(recv_scales, "recv_scales", torch.float32),
-                  _stream())
+    _B.dispatch(ctypes.addressof(h.c), dtype, x, x_scales, recv, recv_scales, _raw_stream(cur), cur)
     return (recv, recv_scales) if dtype != BF16 else recv
 
 
@@ -255,33 +271,17 @@ def dispatch_forward(cfg: Config, topk_idx: torch.Tensor, x: torch.Tensor, dtype
     """Layout + dispatch in one call (README dispatch_forward). Returns
     (handle, recv) or (handle, recv, recv_scales) for the FP8 types."""
     cur = _current_device()
-    idx_dtype = torch.int64 if cfg.idx_bits == 64 else torch.int32
-    shape = topk_idx.shape
-    if len(shape) != 2 or shape[1] != cfg.num_topk:
-        raise ValueError("topk_idx must be [T, %d]" % cfg.num_topk)
-    T, H, R = shape[0], cfg.hidden, cfg.recv_rows_bound()
-    if topk_w is not None and topk_w.shape != shape:
-        raise ValueError("topk_w must match topk_idx")
-    _need(x, (T, H), "x")
-    if dtype == FP8_PREQUANT:
-        _need(x_scales, (T, H // 128), "x_scales")
     if workspace is None:
         workspace = new_workspace(cfg, topk_idx.device)
     fp8 = dtype != BF16
     if recv is None:
-        recv = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=x.device)
+        recv = torch.empty((cfg.recv_rows_bound(), cfg.hidden), dtype=torch.uint8 if fp8 else torch.bfloat16,
+                           device=x.device)
     if fp8 and recv_scales is None:
-        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=x.device)
-    _need(recv, (R, H), "recv")
-    if fp8:
-        _need(recv_scales, (R, H // 128), "recv_scales")
-    xdt = torch.uint8 if dtype == FP8_PREQUANT else torch.bfloat16
-    c = F.ep_dispatch_forward(cfg.c(), T, _dev(topk_idx, "topk_idx", idx_dtype, cur),
-                              _opt(topk_w, "topk_w", torch.float32, cur),
-                              _dev(workspace, "workspace", torch.uint8, cur), workspace.numel(), dtype,
-                              _dev(x, "x", xdt, cur), _opt(x_scales, "x_scales", torch.float32, cur),
-                              _dev(recv, "recv", torch.uint8 if fp8 else torch.bfloat16, cur),
-                              _opt(recv_scales, "recv_scales", torch.float32, cur), _raw_stream(cur))
+        recv_scales = torch.empty((cfg.recv_rows_bound(), cfg.hidden // 128), dtype=torch.float32, device=x.device)
+    c = F.ep_handle()
+    _B.dispatch_forward(cfg.c_addr(), topk_idx, topk_w, workspace, dtype, x, x_scales, recv, recv_scales,
+                        ctypes.addressof(c), _raw_stream(cur), cur)
     h = Handle(cfg, c, workspace, topk_idx)
     return (h, recv, recv_scales) if fp8 else (h, recv)
 
@@ -290,18 +290,11 @@ def combine(h: Handle, y: torch.Tensor, topk_w: Optional[torch.Tensor] = None, o
             row_vals: Optional[torch.Tensor] = None):
     """Returns out [T, H] bf16 (and out_vals [T, k] when row_vals is given)."""
     cur = _current_device()
-    cfg = h.cfg
-    T, H, k, R = h.c.num_tokens, cfg.hidden, cfg.num_topk, cfg.recv_rows_bound()
-    _need(y, (R, H), "y")
-    _need(topk_w, (T, k), "topk_w")
-    _need(row_vals, (R,), "row_vals")
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    _need(out, (T, H), "out")
-    out_vals = None if row_vals is None else torch.empty((T, k), dtype=torch.float32, device=y.device)
-    F.ep_combine(h.c, _dev(y, "y", torch.bfloat16, cur), _opt(topk_w, "topk_w", torch.float32, cur),
-                 _dev(out, "out", torch.bfloat16, cur), _opt(row_vals, "row_vals", torch.float32, cur),
-                 _opt(out_vals, "out_vals", torch.float32, cur), _raw_stream(cur))
+        out = torch.empty((h.c.num_tokens, h.cfg.hidden), dtype=torch.bfloat16, device=y.device)
+    out_vals = None if row_vals is None else torch.empty((h.c.num_tokens, h.cfg.num_topk), dtype=torch.float32,
+                                                         device=y.device)
+    _B.combine(ctypes.addressof(h.c), y, topk_w, out, row_vals, out_vals, _raw_stream(cur), cur)
     return out if row_vals is None else (out, out_vals)
 
 
@@ -309,35 +302,23 @@ def dispatch_backward(h: Handle, grad_recv: torch.Tensor, grad_row_w: Optional[t
                       grad_x: Optional[torch.Tensor] = None, grad_topk_w: Optional[torch.Tensor] = None):
     """README dispatch_backward: returns grad_x (and grad_topk_w when
     grad_row_w is given), into the given buffers or new ones."""
-    T, H, k = h.num_tokens, h.cfg.hidden, h.cfg.num_topk
-    _need(grad_recv, (h.cfg.recv_rows_bound(), H), "grad_recv")
-    _need(grad_row_w, (h.cfg.recv_rows_bound(),), "grad_row_w")
+    cur = _current_device()
+    T, H, k = h.c.num_tokens, h.cfg.hidden, h.cfg.num_topk
     gx = grad_x if grad_x is not None else torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
-    _need(gx, (T, H), "grad_x")
     gw = None
     if grad_row_w is not None:
         gw = grad_topk_w if grad_topk_w is not None else torch.empty((T, k), dtype=torch.float32,
                                                                      device=grad_recv.device)
-        _need(gw, (T, k), "grad_topk_w")
-    F.ep_dispatch_backward(h.c, _dev(grad_recv, "grad_recv", torch.bfloat16),
-                           _opt(grad_row_w, "grad_row_w", torch.float32), _dev(gx, "grad_x", torch.bfloat16),
-                           _opt(gw, "grad_topk_w", torch.float32), _stream())
+    _B.dispatch_backward(ctypes.addressof(h.c), grad_recv, grad_row_w, gx, gw, _raw_stream(cur), cur)
     return gx if gw is None else (gx, gw)
 
 
 def combine_backward(h: Handle, grad_out: torch.Tensor, dtype: int = BF16, topk_w: Optional[torch.Tensor] = None,
                      grad_y: Optional[torch.Tensor] = None, grad_y_scales: Optional[torch.Tensor] = None):
     """README combine_backward: a dispatch of grad_out on the handle."""
-    T, H, R = h.num_tokens, h.cfg.hidden, h.cfg.recv_rows_bound()
-    _need(grad_out, (T, H), "grad_out")
-    _need(topk_w, (T, h.cfg.num_topk), "topk_w")
+    cur = _current_device()
     grad_y, grad_y_scales = _recv_buffers(h, dtype, grad_out.device, grad_y, grad_y_scales)
-    _need(grad_y, (R, H), "grad_y")
-    if dtype != BF16:
-        _need(grad_y_scales, (R, H // 128), "grad_y_scales")
-    F.ep_combine_backward(h.c, dtype, _dev(grad_out, "grad_out", torch.bfloat16),
-                          _opt(topk_w, "topk_w", torch.float32), _dev(grad_y, "grad_y", torch.uint8 if dtype != BF16 else torch.bfloat16),
-                          _opt(grad_y_scales, "grad_y_scales", torch.float32), _stream())
+    _B.combine_backward(ctypes.addressof(h.c), dtype, grad_out, topk_w, grad_y, grad_y_scales, _raw_stream(cur), cur)
     return (grad_y, grad_y_scales) if dtype != BF16 else grad_y
 
 
