@@ -19,8 +19,11 @@ write) over time; `roofline` reports the kernel that moves the most bytes
 against the MI355X HBM peak, timed with HIP events recorded around it
 inside the timed region, on the stream the kernels run on (--graph replays a
 captured step instead; the per-kernel times then come from an evented eager
-pass). `cpu_baseline` times the CPU oracle on the same inputs and the same
-work: its OpenMP build on the host's cores (the value) and its plain build on
+pass); `roofline.pattern_reference` is the simplest kernel with the dominant
+call's access pattern and no arithmetic (libep_ceiling.so), timed in the same
+run on the same rows, which tells how much of that pattern's rate on this
+memory system the kernel reaches. `cpu_baseline` times the CPU oracle on the
+same inputs and the same work: its OpenMP build on the host's cores (the value) and its plain build on
 one core (`single_core`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3] [--step path|forward] [--graph | --bound]
@@ -79,7 +82,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="skip the per-kernel pass with L2 and MALL flushed before each kernel")
     p.add_argument("--no-copy-ceiling", action="store_true",
-                   help="skip timing a plain 1 GiB device-to-device copy for reference")
+                   help="skip the reference kernels: 1 GiB copies and fill, and the dominant call's access pattern "
+                        "with no arithmetic (libep_ceiling.so)")
     return p.parse_args()
 
 
@@ -468,29 +472,75 @@ def main():
         del scratch, sink
 
     copy_ceiling = fill_ceiling = None
+    pattern = None
     if not args.no_copy_ceiling:
-        # Reference only, torch's own kernels on 1 GiB: a device-to-device copy
-        # (read + write) and a fill (a pure write stream, the pattern of the
-        # write-dominated calls).
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-
-        def med_ms(fn):
-            fn()
+        def med_ms(fn, n=5):
+            fn(0)
             torch.cuda.synchronize()
             ts = []
-            for _ in range(5):
+            for i in range(n):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn()
+                fn(i + 1)
                 e1.record(stream)
                 e1.synchronize()
                 ts.append(e0.elapsed_time(e1))
             return float(np.median(ts))
 
-        copy_ceiling = round(2 * (1 << 30) / (med_ms(lambda: b.copy_(a)) * 1e-3) / 1e9, 1)
-        fill_ceiling = round((1 << 30) / (med_ms(lambda: b.fill_(0)) * 1e-3) / 1e9, 1)
+        # Reference only, torch's own kernels on 1 GiB: a device-to-device copy
+        # (read + write) and a fill (a pure write stream).
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        copy_ceiling = round(2 * (1 << 30) / (med_ms(lambda i: b.copy_(a)) * 1e-3) / 1e9, 1)
+        fill_ceiling = round((1 << 30) / (med_ms(lambda i: b.fill_(0)) * 1e-3) / 1e9, 1)
+        # The dominant call's own access pattern with no arithmetic (the
+        # reference kernels of libep_ceiling.so), on the same rows, slots and
+        # rotated sources: what the memory system gives that pattern here.
+        from combine_ep_layout_10_amd import ceiling
+        sp = stream.cuda_stream
+        own_copy = round(2 * (1 << 30) / (med_ms(lambda i: ceiling.copy(a.data_ptr(), b.data_ptr(), 1 << 30, sp))
+                                          * 1e-3) / 1e9, 1)
         del a, b
+        hr = ops.layout(cfg, idx, w, workspace=ws)
+        slots = hr.slot
+        nvalid = int((slots >= 0).sum().item())
+        smax = int(slots.max().item())
+        H2 = 2 * wl.H
+        if dominant in ("dispatch", "combine_backward"):
+            srcs = xs if dominant == "dispatch" else gos
+            dst = recv if dominant == "dispatch" else grad_y
+            drow = wl.H if (dominant == "dispatch" and fp8) else H2
+            ref_bytes = wl.T * H2 + nvalid * drow
+            assert smax < dst.shape[0] and all(t.shape[0] == wl.T for t in srcs)
+            ref_ms = med_ms(lambda i: ceiling.broadcast(srcs[i % len(srcs)].data_ptr(), wl.T, H2, dst.data_ptr(),
+                                                        drow, slots.data_ptr(), wl.k, sp))
+            ref_kernel = "k_broadcast<%d>" % (H2 // drow)
+            wrows = R                  # the receive rows in use
+            what = ("each token's %d-byte row read (plain loads, rotated copies as in the steps) and stored to its %d "
+                    "receive rows of %d bytes (row stores as the path's)" % (H2, wl.k, drow))
+        else:
+            src = y if dominant == "combine" else grad_recv
+            dst = out if dominant == "combine" else grad_x
+            drow = H2
+            ref_bytes = nvalid * H2 + wl.T * H2
+            assert smax < src.shape[0] and dst.shape[0] == wl.T
+            ref_ms = med_ms(lambda i: ceiling.gather(src.data_ptr(), H2, slots.data_ptr(), wl.k, wl.T,
+                                                     dst.data_ptr(), sp))
+            ref_kernel = "k_gather"
+            wrows = wl.T
+            what = ("each token's %d receive rows of %d bytes read (streaming loads) and one row written"
+                    % (wl.k, H2))
+        assert dst.numel() * dst.element_size() >= wrows * drow
+        rw_ms = med_ms(lambda i: ceiling.write_rows(dst.data_ptr(), wrows, drow, sp))
+        ref_gbps = ref_bytes / (ref_ms * 1e-3) / 1e9
+        pattern = {"call": dominant, "kernel": ref_kernel, "pattern": what, "bytes": ref_bytes,
+                   "us": round(ref_ms * 1e3, 2), "GBps": round(ref_gbps, 1),
+                   "frac_of_peak": round(ref_gbps / HBM_PEAK_GBPS, 4),
+                   "dominant_frac_of_reference": round(dom_gbps / ref_gbps, 4),
+                   "row_writes_GBps": round(wrows * drow / (rw_ms * 1e-3) / 1e9, 1),
+                   "copy_4KiB_blocks_1GiB_GBps": own_copy,
+                   "stat": "median of 5 launches after one untimed"}
+        del hr, slots
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -526,11 +576,16 @@ def main():
         kernels[n + "_frac"] = round(gbps[n] / HBM_PEAK_GBPS, 4)
     kernels.update({"bytes": nbytes, "kernel_bytes": {kname[n]: nbytes[n] for n in names}, "kernel_hash": khash,
                     "cold_cache": flushed, "warm": warm, "copy_1GiB_GBps": copy_ceiling,
-                    "fill_1GiB_GBps": fill_ceiling})
+                    "fill_1GiB_GBps": fill_ceiling, "pattern_reference": pattern})
     # the dominant kernel against the rates measured in this run (a device
     # copy: half reads, half writes; a fill: writes only)
     for key, ceil in (("copy", copy_ceiling), ("fill", fill_ceiling)):
         kernels["dominant_frac_of_" + key] = round(dom_gbps / ceil, 4) if ceil else None
+    if pattern is not None:
+        # the dominant kernel against the simplest kernel with its access
+        # pattern, timed in this run on the same rows
+        roofline["pattern_reference"] = {k_: pattern[k_] for k_ in ("kernel", "GBps", "frac_of_peak",
+                                                                    "dominant_frac_of_reference")}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,

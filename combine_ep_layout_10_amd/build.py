@@ -1,4 +1,6 @@
-"""Builds libep.so (the HIP library behind include/ep.h) for gfx950, in-tree.
+"""Builds libep.so (the HIP library behind include/ep.h) for gfx950, in-tree,
+and libep_ceiling.so (access-pattern reference kernels the benchmark times
+beside the path; no part of the API).
 
 Flags: -O3; -ffp-contract=off so that every fused multiply-add in the
 kernels is an explicit one; packed-FP32 instructions disabled (the
@@ -25,8 +27,24 @@ FLAGS = [
 ]
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [HIPCC] + FLAGS + list(extra) + ["-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+CEILING_LIB = os.path.join(HERE, "libep_ceiling.so")
+CEILING_SOURCES = ["ep_ceiling.hip"]
+
+
+def command(out: str = LIB, extra=(), sources=SOURCES) -> list:
+    return [HIPCC] + FLAGS + list(extra) + ["-o", out] + [os.path.join(CSRC, s) for s in sources]
+
+
+def _hipcc(out: str, sources, extra=(), verbose: bool = False) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = command(tmp, extra, sources)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building %s" % os.path.basename(out))
+    os.replace(tmp, out)
 
 
 TORCH_SRC = os.path.join(CSRC, "ep_torch.cpp")
@@ -55,17 +73,10 @@ def build_torch_binding(verbose: bool = False) -> str:
 
 def build(verbose: bool = False, extra=()) -> str:
     """Compile every HIP source into libep.so, then the torch binding that
-    links it (always recompiles both)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp, extra)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libep.so")
-    os.replace(tmp, LIB)
+    links it, then libep_ceiling.so (always recompiles all three)."""
+    _hipcc(LIB, SOURCES, extra, verbose)
     build_torch_binding(verbose)
+    _hipcc(CEILING_LIB, CEILING_SOURCES, (), verbose)
     return LIB
 
 

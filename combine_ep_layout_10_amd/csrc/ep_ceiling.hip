@@ -1,0 +1,167 @@
+// Memory-system ceilings measured beside the path (a measurement aid for
+// the benchmark, built as its own library, libep_ceiling.so; not part of the
+// dispatch/combine API). Each kernel moves bytes in one access pattern and
+// does no arithmetic, so its rate is what the memory system gives that
+// pattern on the box the benchmark runs on:
+//   write_rows  one block per row, the library's streaming row stores
+//               (sc0 sc1 nt), the write stream of the dispatch kinds;
+//   read_rows   one block per row, streaming (nt) loads, the read stream
+//               of the combine kinds;
+//   copy        a plain copy, 4 KiB per 256-thread block, one 16-byte load
+//               and store per lane, plain cache policy;
+//   broadcast   the dispatch's pattern: block t reads its source row (plain
+//               loads) and writes each lane's bytes to the k receive rows
+//               rows[t * k + j] (row -1: skipped) with the row stores above;
+//               a source row may be twice its receive row (the FP8 kinds
+//               read bf16 and write E4M3: the lane then reads 32 bytes and
+//               stores 16);
+//   gather      the combine's pattern: block t reads its k rows
+//               rows[t * k + j] (row -1: skipped) with streaming loads and
+//               writes one row out[t] with plain stores.
+// All sizes are in bytes; rows must be multiples of 16 bytes, at most 2^24.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kFlags = 0x00020000;
+constexpr int kCpolStream = 1 | 2 | 16;  // sc0 nt sc1, as the library's row stores
+constexpr int kCpolNt = 2;
+
+__device__ __forceinline__ void st_row(void* row, uint32_t bytes, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)bytes, kFlags), off, 0,
+                                           kCpolStream);
+}
+
+template <int CPOL>
+__device__ __forceinline__ u32x4 ld_row(const void* row, uint32_t bytes, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)bytes, kFlags), off, 0, CPOL);
+}
+
+__global__ __launch_bounds__(1024) void k_write_rows(char* dst, int row_bytes) {
+    char* row = dst + (int64_t)blockIdx.x * row_bytes;
+    const u32x4 v = {blockIdx.x, threadIdx.x, 1u, 2u};
+    for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x) st_row(row, row_bytes, 16u * c, v);
+}
+
+__global__ __launch_bounds__(1024) void k_read_rows(const char* src, int row_bytes, int32_t* sink) {
+    const char* row = src + (int64_t)blockIdx.x * row_bytes;
+    uint32_t acc = 0;
+    for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x) {
+        const u32x4 v = ld_row<kCpolNt>(row, row_bytes, 16u * c);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = 1;  // keeps the loads; never true for the benchmark's data
+}
+
+__global__ __launch_bounds__(256) void k_copy(const uint4* src, uint4* dst, int64_t nvec) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < nvec) dst[i] = src[i];
+}
+
+template <int RATIO>
+__global__ __launch_bounds__(1024) void k_broadcast(const char* src, int src_bytes, char* dst, int dst_bytes,
+                                                    const int32_t* rows, int k) {
+    const int t = blockIdx.x, c = threadIdx.x, lane = c & 63;
+    const bool act = c < dst_bytes / 16;
+    const char* srow = src + (int64_t)t * src_bytes;
+    u32x4 v = ld_row<0>(srow, src_bytes, act ? 16u * RATIO * c : 0x80000000u);
+    if (RATIO == 2) {
+        const u32x4 v1 = ld_row<0>(srow, src_bytes, act ? 32u * c + 16u : 0x80000000u);
+        v ^= v1;  // the bytes stored depend on both loads
+    }
+    const int my_r = lane < k ? rows[(int64_t)t * k + lane] : -1;
+    for (int j = 0; j < k; ++j) {
+        const int r = __builtin_amdgcn_readlane(my_r, j);
+        if (r >= 0) st_row(dst + (int64_t)r * dst_bytes, dst_bytes, act ? 16u * c : 0x80000000u, v);
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_gather(const char* src, int row_bytes, const int32_t* rows, int k,
+                                                 char* dst) {
+    const int t = blockIdx.x, c = threadIdx.x, lane = c & 63;
+    const uint32_t off = c < row_bytes / 16 ? 16u * c : 0x80000000u;
+    const int my_r = lane < k ? rows[(int64_t)t * k + lane] : -1;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < k; ++j) {
+        const int r = __builtin_amdgcn_readlane(my_r, j);
+        if (r >= 0) acc ^= ld_row<kCpolNt>(src + (int64_t)r * row_bytes, row_bytes, off);
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(
+        acc, __builtin_amdgcn_make_buffer_rsrc(dst + (int64_t)t * row_bytes, 0, row_bytes, kFlags), off, 0, 0);
+}
+
+int threads_for(int row_bytes) {
+    int t = (row_bytes / 16 + 63) / 64 * 64;
+    return t < 64 ? 64 : (t > 1024 ? 1024 : t);
+}
+
+bool row_ok(int64_t rows, int row_bytes) {
+    return rows >= 0 && rows <= 0x7FFFFFFF && row_bytes >= 16 && row_bytes % 16 == 0 && row_bytes <= (1 << 24);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns 0, or a hipError_t value (1 for arguments out of range).
+int ep_ceiling_write_rows(void* dst, int64_t rows, int32_t row_bytes, void* stream) {
+    if (!row_ok(rows, row_bytes) || dst == nullptr) return 1;
+    if (rows == 0) return 0;
+    hipLaunchKernelGGL(k_write_rows, dim3((unsigned)rows), dim3(threads_for(row_bytes)), 0, (hipStream_t)stream,
+                       (char*)dst, row_bytes);
+    return (int)hipGetLastError();
+}
+
+int ep_ceiling_read_rows(const void* src, int64_t rows, int32_t row_bytes, int32_t* sink, void* stream) {
+    if (!row_ok(rows, row_bytes) || src == nullptr || sink == nullptr) return 1;
+    if (rows == 0) return 0;
+    hipLaunchKernelGGL(k_read_rows, dim3((unsigned)rows), dim3(threads_for(row_bytes)), 0, (hipStream_t)stream,
+                       (const char*)src, row_bytes, sink);
+    return (int)hipGetLastError();
+}
+
+int ep_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (src == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0 || bytes / 4096 > 0x7FFFFFFF) return 1;
+    const int64_t nvec = bytes / 16;
+    if (nvec == 0) return 0;
+    hipLaunchKernelGGL(k_copy, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, (uint4*)dst, nvec);
+    return (int)hipGetLastError();
+}
+
+// rows: device [tokens, k] int32, each -1 or a row below the receive
+// buffer's row count (the caller's buffers must hold every row named).
+int ep_ceiling_broadcast(const void* src, int64_t tokens, int32_t src_row_bytes, void* dst, int32_t dst_row_bytes,
+                         const int32_t* rows, int32_t k, void* stream) {
+    if (!row_ok(tokens, src_row_bytes) || !row_ok(0, dst_row_bytes) || src == nullptr || dst == nullptr ||
+        rows == nullptr || k < 1 || k > 64 || dst_row_bytes > 16 * 1024)
+        return 1;
+    const int ratio = src_row_bytes / dst_row_bytes;
+    if ((ratio != 1 && ratio != 2) || src_row_bytes != ratio * dst_row_bytes) return 1;
+    if (tokens == 0) return 0;
+    const dim3 grid((unsigned)tokens), block(threads_for(dst_row_bytes));
+    if (ratio == 1)
+        hipLaunchKernelGGL(k_broadcast<1>, grid, block, 0, (hipStream_t)stream, (const char*)src, src_row_bytes,
+                           (char*)dst, dst_row_bytes, rows, k);
+    else
+        hipLaunchKernelGGL(k_broadcast<2>, grid, block, 0, (hipStream_t)stream, (const char*)src, src_row_bytes,
+                           (char*)dst, dst_row_bytes, rows, k);
+    return (int)hipGetLastError();
+}
+
+// rows: as for ep_ceiling_broadcast; dst holds tokens rows.
+int ep_ceiling_gather(const void* src, int32_t row_bytes, const int32_t* rows, int32_t k, int64_t tokens, void* dst,
+                      void* stream) {
+    if (!row_ok(tokens, row_bytes) || src == nullptr || dst == nullptr || rows == nullptr || k < 1 || k > 64 ||
+        row_bytes > 16 * 1024)
+        return 1;
+    if (tokens == 0) return 0;
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)tokens), dim3(threads_for(row_bytes)), 0, (hipStream_t)stream,
+                       (const char*)src, row_bytes, rows, k, (char*)dst);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"
