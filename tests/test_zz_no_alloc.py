@@ -68,3 +68,64 @@ def test_static_scratch_matches_dispatch_forward():
     _case(1100, 62, cfg, ws_a, ws_b)     # smaller: 9 blocks read only what this call wrote
     _case(300, 63, cfg, ws_a, ws_b)      # 2,400 pairs: the single launch (no partials)
     _case(2000, 64, cfg, ws_a, ws_b)     # larger again after the small ones
+
+
+def test_static_scratch_graph_replay():
+    """The entry point captured in a HIP graph (the use it exists for) at a
+    multi-block layout, whose partials live in the static array: three
+    replays, with new routing, weights and x copied in and eager calls of
+    ep_dispatch_forward between them, each bit-identical to the eager result
+    and its slots equal to the oracle's."""
+    T, H, E, k, A, D = 3000, 512, 256, 8, 128, 8
+    cfg = ops.Config(max_tokens=T, hidden=H, num_experts=E, num_topk=k, num_dests=D, expert_alignment=A)
+    R = cfg.recv_rows_bound()
+    idx_s = torch.zeros((T, k), dtype=torch.int64, device="cuda")
+    w_s = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    x_s = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    recv_s = torch.empty((R, H), dtype=torch.uint8, device="cuda")
+    rs_s = torch.empty((R, H // 128), dtype=torch.float32, device="cuda")
+    ws_g, ws_e = ops.new_workspace(cfg), ops.new_workspace(cfg)
+    c = cfg.c()
+    hc = F.ep_handle()
+
+    def launch():
+        st = F.lib().ep_dispatch_forward_static_scratch(
+            ctypes.byref(c), T, idx_s.data_ptr(), w_s.data_ptr(), ws_g.data_ptr(), ws_g.numel(), ops.FP8_QUANTIZE,
+            x_s.data_ptr(), None, recv_s.data_ptr(), rs_s.data_ptr(), ctypes.byref(hc),
+            torch.cuda.current_stream().cuda_stream)
+        assert st == F.EP_OK, (F.status_string(st), F.last_error_message())
+
+    rng = np.random.default_rng(65)
+    idx_s.copy_(to_dev(random_routing_table(rng, T, E, k)))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch()                                   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    hg = ops.Handle(cfg, hc, ws_g, idx_s)
+    for rep in range(3):
+        log("static scratch graph replay %d" % rep)
+        idx_h = random_routing_table(rng, T, E, k)
+        w_h = rng.random((T, k)).astype(np.float32)
+        x_h = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        idx_s.copy_(to_dev(idx_h))
+        w_s.copy_(to_dev(w_h))
+        x_s.copy_(to_dev_bf16(x_h))
+        recv_s.fill_(0xEE)
+        g.replay()
+        torch.cuda.synchronize()
+        lay = oracle.layout(0, T, E, k, A, D, 0, idx_h, w_h)
+        compare_layout(hg, lay)
+        rows = int(lay["rows"])
+        recv_e = torch.full((R, H), 0xEE, dtype=torch.uint8, device="cuda")
+        rs_e = torch.empty((R, H // 128), dtype=torch.float32, device="cuda")
+        he = _call("ep_dispatch_forward", cfg, idx_s, w_s, x_s, ws_e, recv_e, rs_e)
+        for key in ("cnt", "pad", "expert_off", "dest_off", "dest_tokens", "slot", "err_flags"):
+            assert np.array_equal(host(getattr(hg, key)), host(getattr(he, key))), (rep, key)
+        assert np.array_equal(host(recv_s)[:rows], host(recv_e)[:rows]), rep
+        assert np.array_equal(host(rs_s)[:rows].view(np.uint32), host(rs_e)[:rows].view(np.uint32)), rep
+        assert np.all(host(recv_s)[rows:] == 0xEE), rep
