@@ -22,7 +22,8 @@ captured step instead; the per-kernel times then come from an evented eager
 pass); `roofline.pattern_reference` is the simplest kernel with the dominant
 call's access pattern and no arithmetic (libep_ceiling.so), timed in the same
 run on the same rows, which tells how much of that pattern's rate on this
-memory system the kernel reaches. `cpu_baseline` times the CPU oracle on the
+memory system the kernel reaches (`kernels.pattern_reference` holds the same
+for every call of the step). `cpu_baseline` times the CPU oracle on the
 same inputs and the same work: its OpenMP build on the host's cores (the value) and its plain build on
 one core (`single_core`).
 
@@ -82,8 +83,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="skip the per-kernel pass with L2 and MALL flushed before each kernel")
     p.add_argument("--no-copy-ceiling", action="store_true",
-                   help="skip the reference kernels: 1 GiB copies and fill, and the dominant call's access pattern "
-                        "with no arithmetic (libep_ceiling.so)")
+                   help="skip the reference kernels: 1 GiB copies and fill, and each call's access pattern with no "
+                        "arithmetic (libep_ceiling.so)")
     return p.parse_args()
 
 
@@ -141,10 +142,28 @@ def load_traffic(kernel: str, khash: str, workload: str, path: str = None):
         return None
     with open(path) as f:
         t = json.load(f)
-    ent = t.get(kernel)
+    ent = t.get(workload, {}).get(kernel)
     if not ent or ent.get("kernel_hash") != khash or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
+
+
+def median_event_ms(fn, stream, n: int = 5) -> float:
+    """Median of n launches of fn(i) (i = 1..n, after one untimed fn(0)),
+    each timed with HIP events on `stream`, in ms."""
+    import numpy as np
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(i + 1)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
 
 
 def host_threads() -> int:
@@ -473,19 +492,9 @@ def main():
 
     copy_ceiling = fill_ceiling = None
     pattern = None
-    if not args.no_copy_ceiling:
-        def med_ms(fn, n=5):
-            fn(0)
-            torch.cuda.synchronize()
-            ts = []
-            for i in range(n):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn(i + 1)
-                e1.record(stream)
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            return float(np.median(ts))
+    if not args.no_copy_ceiling and graph is None and bound is None:
+        def med_ms(fn):
+            return median_event_ms(fn, stream)
 
         # Reference only, torch's own kernels on 1 GiB: a device-to-device copy
         # (read + write) and a fill (a pure write stream).
@@ -493,7 +502,7 @@ def main():
         b = torch.empty_like(a)
         copy_ceiling = round(2 * (1 << 30) / (med_ms(lambda i: b.copy_(a)) * 1e-3) / 1e9, 1)
         fill_ceiling = round((1 << 30) / (med_ms(lambda i: b.fill_(0)) * 1e-3) / 1e9, 1)
-        # The dominant call's own access pattern with no arithmetic (the
+        # Each call's own access pattern with no arithmetic (the
         # reference kernels of libep_ceiling.so), on the same rows, slots and
         # rotated sources: what the memory system gives that pattern here.
         from combine_ep_layout_10_amd import ceiling
@@ -506,40 +515,45 @@ def main():
         nvalid = int((slots >= 0).sum().item())
         smax = int(slots.max().item())
         H2 = 2 * wl.H
-        if dominant in ("dispatch", "combine_backward"):
-            srcs = xs if dominant == "dispatch" else gos
-            dst = recv if dominant == "dispatch" else grad_y
-            drow = wl.H if (dominant == "dispatch" and fp8) else H2
-            ref_bytes = wl.T * H2 + nvalid * drow
-            assert smax < dst.shape[0] and all(t.shape[0] == wl.T for t in srcs)
-            ref_ms = med_ms(lambda i: ceiling.broadcast(srcs[i % len(srcs)].data_ptr(), wl.T, H2, dst.data_ptr(),
+
+        def reference(n):
+            """The plain kernel with call n's access pattern on its own rows:
+            (kernel, pattern, bytes, median ms, destination, row bytes, rows)."""
+            if n in ("dispatch", "combine_backward"):
+                srcs = xs if n == "dispatch" else gos
+                dst = recv if n == "dispatch" else grad_y
+                drow = wl.H if (n == "dispatch" and fp8) else H2
+                assert smax < dst.shape[0] and all(t.shape[0] == wl.T for t in srcs)
+                ms = med_ms(lambda i: ceiling.broadcast(srcs[i % len(srcs)].data_ptr(), wl.T, H2, dst.data_ptr(),
                                                         drow, slots.data_ptr(), wl.k, sp))
-            ref_kernel = "k_broadcast<%d>" % (H2 // drow)
-            wrows = R                  # the receive rows in use
-            what = ("each token's %d-byte row read (plain loads, rotated copies as in the steps) and stored to its %d "
-                    "receive rows of %d bytes (row stores as the path's)" % (H2, wl.k, drow))
-        else:
-            src = y if dominant == "combine" else grad_recv
-            dst = out if dominant == "combine" else grad_x
-            drow = H2
-            ref_bytes = nvalid * H2 + wl.T * H2
+                return ("k_broadcast<%d>" % (H2 // drow),
+                        "each token's %d-byte row read (plain loads, rotated copies as in the steps) and stored to "
+                        "its %d receive rows of %d bytes (row stores as the path's)" % (H2, wl.k, drow),
+                        wl.T * H2 + nvalid * drow, ms, dst, drow, R)
+            src = y if n == "combine" else grad_recv
+            dst = out if n == "combine" else grad_x
             assert smax < src.shape[0] and dst.shape[0] == wl.T
-            ref_ms = med_ms(lambda i: ceiling.gather(src.data_ptr(), H2, slots.data_ptr(), wl.k, wl.T,
-                                                     dst.data_ptr(), sp))
-            ref_kernel = "k_gather"
-            wrows = wl.T
-            what = ("each token's %d receive rows of %d bytes read (streaming loads) and one row written"
-                    % (wl.k, H2))
-        assert dst.numel() * dst.element_size() >= wrows * drow
-        rw_ms = med_ms(lambda i: ceiling.write_rows(dst.data_ptr(), wrows, drow, sp))
-        ref_gbps = ref_bytes / (ref_ms * 1e-3) / 1e9
-        pattern = {"call": dominant, "kernel": ref_kernel, "pattern": what, "bytes": ref_bytes,
-                   "us": round(ref_ms * 1e3, 2), "GBps": round(ref_gbps, 1),
-                   "frac_of_peak": round(ref_gbps / HBM_PEAK_GBPS, 4),
-                   "dominant_frac_of_reference": round(dom_gbps / ref_gbps, 4),
-                   "row_writes_GBps": round(wrows * drow / (rw_ms * 1e-3) / 1e9, 1),
-                   "copy_4KiB_blocks_1GiB_GBps": own_copy,
-                   "stat": "median of 5 launches after one untimed"}
+            ms = med_ms(lambda i: ceiling.gather(src.data_ptr(), H2, slots.data_ptr(), wl.k, wl.T, dst.data_ptr(),
+                                                 sp))
+            return ("k_gather", "each token's %d receive rows of %d bytes read (streaming loads) and one row "
+                    "written" % (wl.k, H2), nvalid * H2 + wl.T * H2, ms, dst, H2, wl.T)
+
+        pattern = {}
+        for n in names:
+            ref_kernel, what, ref_bytes, ref_ms, dst, drow, wrows = reference(n)
+            ref_gbps = ref_bytes / (ref_ms * 1e-3) / 1e9
+            kern_gbps = dom_gbps if n == dominant else gbps[n]
+            pattern[n] = {"kernel": ref_kernel, "pattern": what, "bytes": ref_bytes, "us": round(ref_ms * 1e3, 2),
+                          "GBps": round(ref_gbps, 1), "frac_of_peak": round(ref_gbps / HBM_PEAK_GBPS, 4),
+                          "call_frac_of_reference": round(kern_gbps / ref_gbps, 4)}
+            if n == dominant:
+                assert dst.numel() * dst.element_size() >= wrows * drow
+                rw_ms = med_ms(lambda i: ceiling.write_rows(dst.data_ptr(), wrows, drow, sp))
+                pattern[n]["row_writes_GBps"] = round(wrows * drow / (rw_ms * 1e-3) / 1e9, 1)
+                pattern[n]["row_writes_bytes"] = wrows * drow
+        pattern["copy_4KiB_blocks_1GiB_GBps"] = own_copy
+        pattern["stat"] = ("median of 5 launches after one untimed; call_frac_of_reference: the call's rate (the "
+                           "dominant's from the timed region, the others' from the evented pass) over the reference's")
         del hr, slots
 
     cpu = None
@@ -584,8 +598,8 @@ def main():
     if pattern is not None:
         # the dominant kernel against the simplest kernel with its access
         # pattern, timed in this run on the same rows
-        roofline["pattern_reference"] = {k_: pattern[k_] for k_ in ("kernel", "GBps", "frac_of_peak",
-                                                                    "dominant_frac_of_reference")}
+        roofline["pattern_reference"] = {k_: pattern[dominant][k_] for k_ in ("kernel", "GBps", "frac_of_peak",
+                                                                              "call_frac_of_reference")}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -683,6 +697,35 @@ def bench_call(args):
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     khash = kernel_hash()
+    pattern = None
+    if not args.no_copy_ceiling:
+        # the call's access pattern with no arithmetic (libep_ceiling.so), on
+        # the same rows: FP8 backward, each grad_out row (rotated copies)
+        # stored to its pairs' rows at FP8 width; weight_grad, the rows it
+        # reads as plain streams (y's receive rows and grad_out's rows)
+        from combine_ep_layout_10_amd import ceiling
+        sp = stream.cuda_stream
+        slots = h.slot
+        assert int(slots.max().item()) < R_cap
+        if args.step == "fp8_backward":
+            ref_ms = median_event_ms(lambda i: ceiling.broadcast(gos[i % nrot].data_ptr(), T, 2 * H, gq.data_ptr(), H,
+                                                                 slots.data_ptr(), k, sp), stream)
+            ref_bytes = T * 2 * H + P * H
+            ref_kernel, ref_what = "k_broadcast<2>", ("each grad_out row (%d bytes) read and stored to its %d pairs' "
+                                                      "rows of %d bytes" % (2 * H, k, H))
+        else:
+            sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+            ref_ms = median_event_ms(lambda i: (ceiling.read_rows(y.data_ptr(), R, 2 * H, sink.data_ptr(), sp),
+                                                ceiling.read_rows(gos[i % nrot].data_ptr(), T, 2 * H, sink.data_ptr(),
+                                                                  sp)), stream)
+            ref_bytes = (R + T) * 2 * H
+            ref_kernel, ref_what = "k_read_rows", ("the %d receive rows of y and the %d rows of grad_out read "
+                                                   "in order (streaming loads)" % (R, T))
+        ref_gbps = ref_bytes / (ref_ms * 1e-3) / 1e9
+        pattern = {"kernel": ref_kernel, "pattern": ref_what, "bytes": ref_bytes, "us": round(ref_ms * 1e3, 2),
+                   "GBps": round(ref_gbps, 1), "frac_of_peak": round(ref_gbps / HBM_PEAK_GBPS, 4),
+                   "call_frac_of_reference": round(achieved / ref_gbps, 4),
+                   "stat": "median of 5 launches after one untimed"}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -706,7 +749,7 @@ def bench_call(args):
                      "traffic": load_traffic(kname, khash, wl.name + "_" + args.step),
                      "kernel": kname, "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(launch_ms * 1e3, 2), "timed": "events in the timed region",
-                     "inputs": "grad_out cycled through %d copies" % nrot},
+                     "inputs": "grad_out cycled through %d copies" % nrot, "pattern_reference": pattern},
         "cpu_baseline": cpu,
         "kernels": {"kernel_bytes": {kname: nbytes}, "kernel_hash": khash, "pairs": P, "rows": R},
     }

@@ -22,7 +22,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace ep_ceiling {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFlags = 0x00020000;
@@ -102,7 +102,9 @@ bool row_ok(int64_t rows, int row_bytes) {
     return rows >= 0 && rows <= 0x7FFFFFFF && row_bytes >= 16 && row_bytes % 16 == 0 && row_bytes <= (1 << 24);
 }
 
-}  // namespace
+}  // namespace ep_ceiling
+
+using namespace ep_ceiling;
 
 extern "C" {
 

@@ -14,8 +14,9 @@ Two reports, both written as short text under profiles/:
            `bench.py` reports for the same workload (for the grouped GEMM:
            its HBM floor, weights and A read once, output written once), and
            also stored in
-           profiles/traffic.json, which `bench.py` reads for
-           `roofline.traffic` while the kernel sources are unchanged.
+           profiles/traffic.json (by workload, then kernel), which
+           `bench.py` reads for `roofline.traffic` while the kernel sources
+           are unchanged.
 
     python -m combine_ep_layout_10_amd.profile_summary trace STATS_CSV --workload v3 \\
         --command "..." --bench-json BENCH.json --out profiles/NAME.md
@@ -33,6 +34,7 @@ import os
 import re
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+REF_NS = "ep_ceiling::"
 GIB = 1 << 30
 
 
@@ -112,7 +114,7 @@ def cmd_trace(a) -> None:
         lines += ["Kernel sources hash (as bench.py reports it): `%s`" % bench["kernels"]["kernel_hash"], ""]
     lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for name, calls, avg, mn, mx in sorted(rows, key=lambda r: -r[1] * r[2]):
-        if not name.startswith("ep::") and not a.all:
+        if not (name.startswith("ep::") or name.startswith(REF_NS)) and not a.all:
             continue
         lines.append("| %s | %d | %.2f | %.2f | %.2f |" % (name, calls, avg, mn, mx))
     with open(a.out, "w") as f:
@@ -130,9 +132,20 @@ def cmd_traffic(a) -> None:
     # algorithmic (or least) bytes per launch of each kernel the bench line
     # measures: the path's calls, or the grouped GEMM's HBM floor
     alg = dict(bench["kernels"].get("kernel_bytes", {}))
+    stored = set(alg)
+    # the access-pattern reference kernels the bench line timed beside the
+    # path (libep_ceiling.so), against the bytes it credits them with
+    ref = bench["kernels"].get("pattern_reference") or {}
+    for v in ref.values():
+        if isinstance(v, dict):
+            alg.setdefault(REF_NS + v["kernel"], v["bytes"])
+            if "row_writes_bytes" in v:
+                alg[REF_NS + "k_write_rows"] = v["row_writes_bytes"]
+    if ref:
+        alg[REF_NS + "k_copy"] = 2 * GIB
     table = {}
     for name in sorted(set(fetch) | set(write)):
-        if not name.startswith("ep::"):
+        if not name.startswith("ep::") and kernel_key(name) not in alg:
             continue
         fk = [v for _, v in fetch.get(name, [])]
         wk = [v for _, v in write.get(name, [])]
@@ -160,11 +173,12 @@ def cmd_traffic(a) -> None:
         al = alg.get(key)
         ratio = "%.3f" % (nbytes / al) if al else "-"
         lines.append("| %s | %.1f | %.1f | %d | %s | %s |" % (name, f_kib, w_kib, nbytes, al if al else "-", ratio))
-        if key not in alg:
-            continue  # set-up kernels of this run (e.g. the dispatch before a GEMM): listed, not stored
-        out_json[key] = {"bytes_per_launch": nbytes, "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
-                         "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "kernel_hash": khash,
-                         "workload": a.workload}
+        if key not in stored:
+            continue  # set-up and reference kernels of this run: listed, not stored
+        # by workload, then kernel: one kernel runs in several workloads' steps
+        out_json.setdefault(a.workload, {})[key] = {
+            "bytes_per_launch": nbytes, "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "kernel_hash": khash, "workload": a.workload}
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     if a.json:

@@ -67,16 +67,18 @@ def test_traffic_scaling_and_recorded_kernels(tmp_path):
     line = {"kernels": {"kernel_hash": "abc", "kernel_bytes": {"k_dispatch<1>": 7_000_000}}}
     (tmp_path / "b.log").write_text("[bench] noise\n" + json.dumps(line) + "\n")
     out_json = tmp_path / "traffic.json"
-    out_json.write_text(json.dumps({"k_combine<true>": {"bytes_per_launch": 1, "kernel_hash": "old"}}))
+    out_json.write_text(json.dumps({"w": {"k_combine<true>": {"bytes_per_launch": 1, "kernel_hash": "old"}},
+                                    "v": {"k_dispatch<1>": {"bytes_per_launch": 2, "kernel_hash": "abc"}}}))
     ps.main(["traffic", "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
              "--workload", "w", "--command-fetch", "cf", "--command-write", "cw",
              "--bench-json", str(tmp_path / "b.log"), "--out", str(tmp_path / "t.md"), "--json", str(out_json)])
     t = json.loads(out_json.read_text())
-    assert set(t) == {"k_combine<true>", "k_dispatch<1>"}        # set-up kernel listed in the table, not stored
-    e = t["k_dispatch<1>"]
+    assert set(t["w"]) == {"k_combine<true>", "k_dispatch<1>"}   # set-up kernel listed in the table, not stored
+    e = t["w"]["k_dispatch<1>"]
     assert e["kernel_hash"] == "abc" and e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
     assert e["bytes_per_launch"] == round((1001.0 * 2 + 5000.0) * 1024)
-    assert t["k_combine<true>"]["kernel_hash"] == "old"          # other entries are kept
+    assert t["w"]["k_combine<true>"]["kernel_hash"] == "old"     # other entries are kept
+    assert t["v"]["k_dispatch<1>"]["bytes_per_launch"] == 2       # the same kernel in another workload too
     md = (tmp_path / "t.md").read_text()
     assert "ep::k_layout_count" in md and "| 7000000 |" in md
 
@@ -122,13 +124,39 @@ def test_kernel_hash_tracks_step_sources():
             assert os.path.exists(os.path.join(bench.ROOT, "combine_ep_layout_10_amd", "csrc", f)), (step, f)
 
 
+def test_traffic_lists_reference_kernels(tmp_path):
+    """The access-pattern reference kernels of the bench line are listed
+    against the bytes the line credits them with, and never stored."""
+    copy = "__amd_rocclr_copyBuffer"
+    bc = "void ep_ceiling::k_broadcast<1>(char const*, int, char*, int, int const*, int)"
+    wr = "void ep_ceiling::k_write_rows(char*, int)"
+    gib_kib = (1 << 30) / 1024
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 1 << 20, gib_kib / 2), (bc, 9, 500.0), (wr, 9, 0.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1 << 20, gib_kib), (bc, 9, 4000.0), (wr, 9, 2000.0)])
+    ref = {"combine_backward": {"kernel": "k_broadcast<1>", "bytes": 5000 * 1024, "row_writes_bytes": 2000 * 1024},
+           "stat": "x"}
+    line = {"kernels": {"kernel_hash": "abc", "kernel_bytes": {"k_dispatch<1>": 7}, "pattern_reference": ref}}
+    (tmp_path / "b.log").write_text(json.dumps(line) + "\n")
+    out_json = tmp_path / "traffic.json"
+    ps.main(["traffic", "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
+             "--workload", "w", "--command-fetch", "cf", "--command-write", "cw",
+             "--bench-json", str(tmp_path / "b.log"), "--out", str(tmp_path / "t.md"), "--json", str(out_json)])
+    md = (tmp_path / "t.md").read_text()
+    assert "| ep_ceiling::k_broadcast<1> | 500.0 | 4000.0 | %d | %d | 1.000 |" % (5000 * 1024, 5000 * 1024) in md
+    assert "| ep_ceiling::k_write_rows | 0.0 | 2000.0 |" in md
+    assert json.loads(out_json.read_text()) == {}
+
+
 def test_traffic_only_for_the_measured_workload_and_sources(tmp_path):
     """Counter bytes are reported only for the workload and kernel sources
     they were taken on: a launch's bytes depend on its shape."""
     p = tmp_path / "traffic.json"
-    p.write_text(json.dumps({"k_combine<true>": {"bytes_per_launch": 123, "kernel_hash": "abc",
-                                                 "workload": "v3"}}))
+    p.write_text(json.dumps({"v3": {"k_combine<true>": {"bytes_per_launch": 123, "kernel_hash": "abc",
+                                                        "workload": "v3"}},
+                             "mid": {"k_combine<true>": {"bytes_per_launch": 45, "kernel_hash": "abc",
+                                                         "workload": "mid"}}}))
     assert bench.load_traffic("k_combine<true>", "abc", "v3", str(p)) == 123
+    assert bench.load_traffic("k_combine<true>", "abc", "mid", str(p)) == 45
     assert bench.load_traffic("k_combine<true>", "abc", "decode", str(p)) is None
     assert bench.load_traffic("k_combine<true>", "abd", "v3", str(p)) is None
     assert bench.load_traffic("k_combine<false>", "abc", "v3", str(p)) is None
