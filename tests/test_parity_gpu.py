@@ -20,14 +20,19 @@ if torch.cuda.is_available():
 
 
 def _run_small(T, H, E, k, A=1, D=1, C=0, mode=0, seed=0, masked=0.0, bad=0.0, distinct=True,
-               idx_bits=64, flags=0, dispatch="bf16", weights=True, forward=False):
+               idx_bits=64, flags=0, dispatch="bf16", weights=True, forward=False, table=None):
     """Random small case through every stage, checked against the oracle.
     forward=True builds the layout and dispatches with one ep_dispatch_forward
-    call instead of ep_layout + ep_dispatch."""
-    log("case T=%d H=%d E=%d k=%d A=%d D=%d C=%d mode=%d idx_bits=%d dispatch=%s seed=%d forward=%d"
-        % (T, H, E, k, A, D, C, mode, idx_bits, dispatch, seed, forward))
+    call instead of ep_layout + ep_dispatch; table: a given routing table
+    instead of a random one."""
+    log("case T=%d H=%d E=%d k=%d A=%d D=%d C=%d mode=%d idx_bits=%d dispatch=%s seed=%d forward=%d table=%s"
+        % (T, H, E, k, A, D, C, mode, idx_bits, dispatch, seed, forward, table is not None))
     rng = np.random.default_rng(seed)
-    idx = random_routing_table(rng, T, E, k, masked_frac=masked, bad_frac=bad, distinct=distinct)
+    if table is None:
+        idx = random_routing_table(rng, T, E, k, masked_frac=masked, bad_frac=bad, distinct=distinct)
+    else:
+        idx = np.ascontiguousarray(table, dtype=np.int64)
+        assert idx.shape == (T, k)
     if idx_bits == 32:
         idx = idx.astype(np.int32)
     w = rng.random((T, k)).astype(np.float32) if weights else None
@@ -213,6 +218,25 @@ def test_largest_topk_and_ragged_rows(T, H, E, k, A, D, dispatch):
     _run_small(T, H, E, k, A=A, D=D, seed=T + H, dispatch=dispatch)
     _run_small(T, H, E, k, A=A, D=D, seed=T + H + 1, dispatch=dispatch, forward=True, masked=0.2, bad=0.05,
                distinct=False)
+
+
+def test_hot_experts():
+    """Degenerate routing at sizes that take the multi-block layout: every
+    token to the same k experts (one expert's count is T, the others 0),
+    to the last destination's experts, and half of the batch to one hot
+    set; the single launch with every token on the same experts; FIXED
+    capacity with every token on the same experts (all but C pairs of each
+    dropped)."""
+    T, E, k = 5000, 256, 8
+    same = np.tile(np.arange(k), (T, 1))
+    _run_small(T, 256, E, k, A=128, D=8, seed=81, table=same)
+    _run_small(T, 256, E, k, A=128, D=8, seed=82, table=same[:, ::-1] + (E - k), dispatch="fp8")
+    rng = np.random.default_rng(83)
+    half = random_routing_table(rng, T, E, k)
+    half[::2] = np.arange(100, 100 + k)
+    _run_small(T, 256, E, k, A=128, D=8, seed=84, table=half, dispatch="fp8")
+    _run_small(300, 512, E, k, A=1, seed=85, table=same[:300], forward=True, dispatch="fp8")
+    _run_small(T, 256, E, k, mode=oracle.MODE_FIXED, C=128, seed=86, table=same)
 
 
 def test_masked_and_bad_ids():
