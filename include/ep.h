@@ -22,7 +22,10 @@
  *     device can access); "host" pointers are ordinary host memory.
  *   - The caller owns every buffer: inputs, outputs and the workspace. The
  *     library allocates no device memory, keeps no pointer after returning
- *     and holds no global state except a thread-local error message.
+ *     and holds no global state except a thread-local error message, each
+ *     device's CU count (queried once) and the fixed 1 MiB device array of
+ *     ep_dispatch_forward_static_scratch (one per GPU, for the process's
+ *     lifetime).
  *   - `stream` is a hipStream_t (NULL = the null stream). All work is
  *     enqueued on it and runs asynchronously; only ep_handle_read_counts and
  *     ep_handle_check wait for the stream.
