@@ -86,7 +86,7 @@ _SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P]),
     "ep_combine": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, _P]),
-    "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P]),
+    "ep_combine_backward": (ctypes.c_int, [ctypes.POINTER(ep_handle), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "ep_combine_weight_grad": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
     "ep_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [ctypes.POINTER(ep_handle), _P, _P, _P, _P]),
@@ -170,10 +170,10 @@ def ep_dispatch_backward(h: ep_handle, grad_recv: int, grad_row_w, grad_x: int, 
            "ep_dispatch_backward")
 
 
-def ep_combine_backward(h: ep_handle, dtype: int, grad_out: int, topk_w, grad_y: int, grad_y_scales,
-                        stream: int) -> None:
-    _check(lib().ep_combine_backward(ctypes.byref(h), int(dtype), grad_out, topk_w, grad_y, grad_y_scales,
-                                     stream), "ep_combine_backward")
+def ep_combine_backward(h: ep_handle, dtype: int, grad_out: int, grad_out_scales, topk_w, grad_y: int,
+                        grad_y_scales, stream: int) -> None:
+    _check(lib().ep_combine_backward(ctypes.byref(h), int(dtype), grad_out, grad_out_scales, topk_w, grad_y,
+                                     grad_y_scales, stream), "ep_combine_backward")
 
 
 def ep_combine_weight_grad(h: ep_handle, grad_out: int, y: int, grad_topk_w: int, stream: int) -> None:

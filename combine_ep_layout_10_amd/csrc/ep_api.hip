@@ -487,11 +487,11 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
     return do_combine(h, grad_recv, nullptr, grad_x, grad_row_w, grad_topk_w, (hipStream_t)stream);
 }
 
-ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* grad_out, const float* topk_w,
-                              void* grad_y, float* grad_y_scales, void* stream) {
+ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* grad_out, const float* grad_out_scales,
+                              const float* topk_w, void* grad_y, float* grad_y_scales, void* stream) {
     if (topk_w != nullptr && dtype == EP_FP8_PREQUANT)
         return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward needs EP_BF16 or EP_FP8_QUANTIZE");
-    return do_dispatch(h, dtype, grad_out, nullptr, topk_w, grad_y, grad_y_scales, (hipStream_t)stream);
+    return do_dispatch(h, dtype, grad_out, grad_out_scales, topk_w, grad_y, grad_y_scales, (hipStream_t)stream);
 }
 
 ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const void* y, float* grad_topk_w,

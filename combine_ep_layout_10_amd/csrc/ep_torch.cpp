@@ -110,7 +110,8 @@ void dispatch_forward(int64_t cfg, const at::Tensor& topk_idx, const c10::option
 }
 
 // ep_dispatch (pair_w absent) and ep_combine_backward (pair_w = topk_w):
-// both move a [T, H] input into the receive rows of the handle.
+// both move a [T, H] input (with its 1x128 scales when pre-quantised) into
+// the receive rows of the handle.
 void dispatch_like(int64_t handle, int64_t dtype, const at::Tensor& x, const c10::optional<at::Tensor>& x_scales,
                    const c10::optional<at::Tensor>& pair_w, const at::Tensor& recv,
                    const c10::optional<at::Tensor>& recv_scales, bool backward, int64_t stream, int64_t dev) {
@@ -119,21 +120,20 @@ void dispatch_like(int64_t handle, int64_t dtype, const at::Tensor& x, const c10
     const int64_t T = h->num_tokens, H = c->hidden, R = rows_bound(c);
     const bool fp8 = dtype != EP_BF16, pre = dtype == EP_FP8_PREQUANT;
     shape(x, {T, H}, backward ? "grad_out" : "x");
-    if (pre) opt_shape(x_scales, {T, H / 128}, "x_scales");
+    if (pre) opt_shape(x_scales, {T, H / 128}, backward ? "grad_out_scales" : "x_scales");
     opt_shape(pair_w, {T, c->num_topk}, "topk_w");
     shape(recv, {R, H}, backward ? "grad_y" : "recv");
     if (fp8) opt_shape(recv_scales, {R, H / 128}, backward ? "grad_y_scales" : "recv_scales");
     void* px = ptr(x, backward ? "grad_out" : "x", pre ? at::kByte : at::kBFloat16, dev);
     void* pr = ptr(recv, backward ? "grad_y" : "recv", fp8 ? at::kByte : at::kBFloat16, dev);
     float* prs = (float*)opt_ptr(recv_scales, backward ? "grad_y_scales" : "recv_scales", at::kFloat, dev);
+    const float* pxs = (const float*)opt_ptr(x_scales, backward ? "grad_out_scales" : "x_scales", at::kFloat, dev);
     if (backward)
-        ok(ep_combine_backward(h, (int32_t)dtype, px, (const float*)opt_ptr(pair_w, "topk_w", at::kFloat, dev), pr,
-                               prs, stream_of(stream)),
+        ok(ep_combine_backward(h, (int32_t)dtype, px, pxs, (const float*)opt_ptr(pair_w, "topk_w", at::kFloat, dev),
+                               pr, prs, stream_of(stream)),
            "ep_combine_backward");
     else
-        ok(ep_dispatch(h, (int32_t)dtype, px, (const float*)opt_ptr(x_scales, "x_scales", at::kFloat, dev), pr, prs,
-                       stream_of(stream)),
-           "ep_dispatch");
+        ok(ep_dispatch(h, (int32_t)dtype, px, pxs, pr, prs, stream_of(stream)), "ep_dispatch");
 }
 
 void dispatch(int64_t handle, int64_t dtype, const at::Tensor& x, const c10::optional<at::Tensor>& x_scales,
@@ -142,9 +142,10 @@ void dispatch(int64_t handle, int64_t dtype, const at::Tensor& x, const c10::opt
 }
 
 void combine_backward(int64_t handle, int64_t dtype, const at::Tensor& grad_out,
-                      const c10::optional<at::Tensor>& topk_w, const at::Tensor& grad_y,
-                      const c10::optional<at::Tensor>& grad_y_scales, int64_t stream, int64_t dev) {
-    dispatch_like(handle, dtype, grad_out, c10::nullopt, topk_w, grad_y, grad_y_scales, true, stream, dev);
+                      const c10::optional<at::Tensor>& grad_out_scales, const c10::optional<at::Tensor>& topk_w,
+                      const at::Tensor& grad_y, const c10::optional<at::Tensor>& grad_y_scales, int64_t stream,
+                      int64_t dev) {
+    dispatch_like(handle, dtype, grad_out, grad_out_scales, topk_w, grad_y, grad_y_scales, true, stream, dev);
 }
 
 // ep_combine (weights optional) and ep_dispatch_backward (no weights): a

@@ -314,11 +314,15 @@ def dispatch_backward(h: Handle, grad_recv: torch.Tensor, grad_row_w: Optional[t
 
 
 def combine_backward(h: Handle, grad_out: torch.Tensor, dtype: int = BF16, topk_w: Optional[torch.Tensor] = None,
-                     grad_y: Optional[torch.Tensor] = None, grad_y_scales: Optional[torch.Tensor] = None):
-    """README combine_backward: a dispatch of grad_out on the handle."""
+                     grad_y: Optional[torch.Tensor] = None, grad_y_scales: Optional[torch.Tensor] = None,
+                     grad_out_scales: Optional[torch.Tensor] = None):
+    """README combine_backward: a dispatch of grad_out on the handle
+    (FP8_PREQUANT: grad_out holds E4M3 codes and grad_out_scales their 1x128
+    scales, the README's (data, scale_factors) input)."""
     cur = _current_device()
     grad_y, grad_y_scales = _recv_buffers(h, dtype, grad_out.device, grad_y, grad_y_scales)
-    _B.combine_backward(ctypes.addressof(h.c), dtype, grad_out, topk_w, grad_y, grad_y_scales, _raw_stream(cur), cur)
+    _B.combine_backward(ctypes.addressof(h.c), dtype, grad_out, grad_out_scales, topk_w, grad_y, grad_y_scales,
+                        _raw_stream(cur), cur)
     return (grad_y, grad_y_scales) if dtype != BF16 else grad_y
 
 

@@ -270,15 +270,19 @@ ep_status ep_dispatch_backward(const ep_handle* h, const void* grad_recv, const 
                                void* grad_x, float* grad_topk_w, void* stream);
 
 /* README combine_backward: the backward of a combine is a dispatch of the
- * output gradient on the same handle. With topk_w, the copy for pair (t, j)
- * is the gradient of the weighted combine, bf16(topk_w[t, j] *
- * float(grad_out[t, c])) (one binary32 multiply, round to nearest even);
- * with EP_FP8_QUANTIZE that BF16 copy is then quantised per 1x128 block as
- * ep_dispatch quantises x, each pair with its own scales. EP_FP8_PREQUANT
- * with topk_w returns EP_ERR_UNSUPPORTED. */
+ * output gradient on the same handle, which the README lets arrive in BF16
+ * or as an FP8 (data, scale_factors) pair. dtype, grad_out, grad_out_scales,
+ * grad_y and grad_y_scales are as ep_dispatch's dtype, x, x_scales, recv and
+ * recv_scales (grad_out_scales: EP_FP8_PREQUANT only, device [T, hidden/128]
+ * binary32; NULL otherwise). With topk_w, the copy for pair (t, j) is the
+ * gradient of the weighted combine, bf16(topk_w[t, j] * float(grad_out[t, c]))
+ * (one binary32 multiply, round to nearest even); with EP_FP8_QUANTIZE that
+ * BF16 copy is then quantised per 1x128 block as ep_dispatch quantises x,
+ * each pair with its own scales. EP_FP8_PREQUANT with topk_w returns
+ * EP_ERR_UNSUPPORTED (weighting codes would need them re-quantised). */
 ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* grad_out,
-                              const float* topk_w, void* grad_y, float* grad_y_scales,
-                              void* stream);
+                              const float* grad_out_scales, const float* topk_w, void* grad_y,
+                              float* grad_y_scales, void* stream);
 
 /* Gradient of the weighted combine with respect to its weights (the part of
  * README combine_backward that a weighted combine adds; the gradient with

@@ -108,10 +108,12 @@ def test_dispatch_combine_argument_errors():
     assert lib.ep_dispatch(ctypes.byref(h2), F.EP_FP8_QUANTIZE, fake, None, fake, fake, None) == F.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(h), None, None, fake, None, None, None) == F.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(h), fake, None, fake, fake, None, None) == F.EP_ERR_INVALID_ARG
-    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_PREQUANT, fake, fake, fake, fake,
+    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_PREQUANT, fake, fake, fake, fake, fake,
                                    None) == F.EP_ERR_UNSUPPORTED                # weights with FP8 input
-    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_QUANTIZE, fake, fake, fake, None,
-                                   None) == F.EP_ERR_INVALID_ARG                # scales missing
+    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_QUANTIZE, fake, None, fake, fake, None,
+                                   None) == F.EP_ERR_INVALID_ARG                # output scales missing
+    assert lib.ep_combine_backward(ctypes.byref(h), F.EP_FP8_PREQUANT, fake, None, None, fake, fake,
+                                   None) == F.EP_ERR_INVALID_ARG                # input scales missing
     assert lib.ep_combine_weight_grad(ctypes.byref(h), None, fake, fake, None) == F.EP_ERR_INVALID_ARG
     assert lib.ep_combine_weight_grad(ctypes.byref(h), fake, None, fake, None) == F.EP_ERR_INVALID_ARG
     assert lib.ep_combine_weight_grad(ctypes.byref(h), fake, fake, None, None) == F.EP_ERR_INVALID_ARG

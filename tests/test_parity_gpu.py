@@ -481,6 +481,16 @@ def test_backward_duals():
     assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
     with pytest.raises(Exception):
         ops.combine_backward(h, to_dev(np.zeros((T, H), np.uint8)), ops.FP8_PREQUANT, to_dev(w))
+    # an FP8 (codes, scales) gradient, unweighted: every code byte (NaN
+    # patterns included) and scale lands in its pairs' rows bitwise
+    gq8 = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    gs8 = rng.standard_normal((T, H // 128)).astype(np.float32)
+    q, s = oracle.dispatch_fp8_prequant(lay, gq8, gs8, k)
+    gq, gs = ops.combine_backward(h, to_dev(gq8), ops.FP8_PREQUANT, grad_out_scales=to_dev(gs8))
+    assert np.array_equal(host(gq)[rows], q[rows])
+    assert np.array_equal(host(gs)[rows].view(np.uint32), s[rows].view(np.uint32))
+    with pytest.raises(Exception):
+        ops.combine_backward(h, to_dev(gq8), ops.FP8_PREQUANT)          # scales missing
 
 
 def _weight_grad_bound(H, g, y, slot):
