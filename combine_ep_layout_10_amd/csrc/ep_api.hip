@@ -112,8 +112,17 @@ ep_status check_handle(const ep_handle* h) {
 }
 
 // Checks a dispatch and fills its kernel arguments; enqueues nothing.
+// `names`: what the caller calls its input, scales, output and output scales
+// (ep_dispatch's, or ep_combine_backward's), for the error messages.
+struct DispatchNames {
+    const char *x, *x_scales, *recv, *recv_scales;
+};
+constexpr DispatchNames kDispatchNames = {"x", "x_scales", "recv", "recv_scales"};
+constexpr DispatchNames kCombineBackwardNames = {"grad_out", "grad_out_scales", "grad_y", "grad_y_scales"};
+
 ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales,
-                           const float* pair_w, void* recv, float* recv_scales, ep::DispatchArgs* out, int* kind) {
+                           const float* pair_w, void* recv, float* recv_scales, ep::DispatchArgs* out, int* kind,
+                           const DispatchNames& n = kDispatchNames) {
     ep_status s = check_handle(h);
     if (s != EP_OK) return s;
     const ep_config& c = h->cfg;
@@ -125,12 +134,14 @@ ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, con
         return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)", c.hidden);
     if (pair_w != nullptr && dtype == EP_FP8_PREQUANT)
         return fail(EP_ERR_UNSUPPORTED, "per-pair weights need EP_BF16 or EP_FP8_QUANTIZE");
-    if (T > 0 && (x == nullptr || !aligned(x, 16))) return fail(EP_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
-    if (recv == nullptr || !aligned(recv, 16)) return fail(EP_ERR_INVALID_ARG, "recv must be non-NULL and 16-byte aligned");
+    if (T > 0 && (x == nullptr || !aligned(x, 16)))
+        return fail(EP_ERR_INVALID_ARG, "%s must be non-NULL and 16-byte aligned", n.x);
+    if (recv == nullptr || !aligned(recv, 16))
+        return fail(EP_ERR_INVALID_ARG, "%s must be non-NULL and 16-byte aligned", n.recv);
     if (fp8 && (recv_scales == nullptr || !aligned(recv_scales, 4)))
-        return fail(EP_ERR_INVALID_ARG, "recv_scales is required for FP8 dispatch");
+        return fail(EP_ERR_INVALID_ARG, "%s (4-byte aligned) is required for an FP8 output", n.recv_scales);
     if (dtype == EP_FP8_PREQUANT && T > 0 && (x_scales == nullptr || !aligned(x_scales, 4)))
-        return fail(EP_ERR_INVALID_ARG, "x_scales is required for EP_FP8_PREQUANT");
+        return fail(EP_ERR_INVALID_ARG, "%s (4-byte aligned) is required for EP_FP8_PREQUANT", n.x_scales);
     ep::DispatchArgs& a = *out;
     a.x = x;
     a.x_scales = x_scales;
@@ -158,10 +169,10 @@ ep_status prepare_dispatch(const ep_handle* h, int32_t dtype, const void* x, con
 }
 
 ep_status do_dispatch(const ep_handle* h, int32_t dtype, const void* x, const float* x_scales, const float* pair_w,
-                      void* recv, float* recv_scales, hipStream_t stream) {
+                      void* recv, float* recv_scales, hipStream_t stream, const DispatchNames& n = kDispatchNames) {
     ep::DispatchArgs a;
     int kind = 0;
-    ep_status s = prepare_dispatch(h, dtype, x, x_scales, pair_w, recv, recv_scales, &a, &kind);
+    ep_status s = prepare_dispatch(h, dtype, x, x_scales, pair_w, recv, recv_scales, &a, &kind, n);
     if (s != EP_OK) return s;
     hipError_t e = ep::launch_dispatch(kind, a, stream);
     if (e != hipSuccess) return hip_fail(e, "dispatch launch");
@@ -491,7 +502,8 @@ ep_status ep_combine_backward(const ep_handle* h, int32_t dtype, const void* gra
                               const float* topk_w, void* grad_y, float* grad_y_scales, void* stream) {
     if (topk_w != nullptr && dtype == EP_FP8_PREQUANT)
         return fail(EP_ERR_UNSUPPORTED, "weighted combine_backward needs EP_BF16 or EP_FP8_QUANTIZE");
-    return do_dispatch(h, dtype, grad_out, grad_out_scales, topk_w, grad_y, grad_y_scales, (hipStream_t)stream);
+    return do_dispatch(h, dtype, grad_out, grad_out_scales, topk_w, grad_y, grad_y_scales, (hipStream_t)stream,
+                       kCombineBackwardNames);
 }
 
 ep_status ep_combine_weight_grad(const ep_handle* h, const void* grad_out, const void* y, float* grad_topk_w,
