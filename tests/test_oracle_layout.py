@@ -187,3 +187,39 @@ def test_argument_checks():
         oracle.layout(0, 2, 6, 2, 0, 1, 0, np.zeros((2, 2), np.int64))  # A < 1
     with pytest.raises(ValueError):
         oracle.layout(1, 2, 6, 2, 1, 1, 0, np.zeros((2, 2), np.int64))  # C < 1
+
+
+try:
+    from hypothesis import given, settings, HealthCheck, strategies as st
+except ImportError:  # pragma: no cover - hypothesis is installed in this image
+    given = None
+
+if given is not None:
+    @st.composite
+    def _layout_case(draw):
+        """A routing table with masked (-1) and out-of-range ids, any D that
+        divides E, either mode, small enough for the O(P^2) definition."""
+        T = draw(st.integers(0, 12))
+        k = draw(st.integers(1, 4))
+        E = draw(st.sampled_from([1, 2, 3, 4, 6, 8]))
+        D = draw(st.sampled_from([d for d in range(1, E + 1) if E % d == 0]))
+        mode = draw(st.sampled_from([oracle.MODE_COMPACT, oracle.MODE_FIXED]))
+        A = draw(st.integers(1, 6)) if mode == oracle.MODE_COMPACT else 1
+        C = draw(st.integers(1, 5)) if mode == oracle.MODE_FIXED else 0
+        ids = draw(st.lists(st.integers(-1, E + 1), min_size=T * k, max_size=T * k))
+        return mode, T, E, k, A, D, C, np.array(ids, np.int64).reshape(T, k)
+
+    @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+    @given(_layout_case())
+    def test_layout_matches_definition_on_random_tables(case):
+        """Property form of the brute-force pin: every drawn table (duplicate
+        experts within a token allowed, masked and bad ids mixed in) gives
+        the definition's counts, offsets, slots and flags, and the same
+        layout from int32 ids."""
+        mode, T, E, k, A, D, C, idx = case
+        lay = check_against_brute(mode, T, E, k, A, D, C, idx)
+        bf = brute_force_layout(mode, T, E, k, A, D, C, idx)
+        assert lay["flags"] == bf["flags"]
+        lay32 = oracle.layout(mode, T, E, k, A, D, C, idx.astype(np.int32))
+        for key in ("cnt", "pad", "expert_off", "slot", "dest_tokens", "dest_off"):
+            assert np.array_equal(lay[key], lay32[key]), key
