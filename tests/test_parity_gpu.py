@@ -220,6 +220,31 @@ def test_largest_topk_and_ragged_rows(T, H, E, k, A, D, dispatch):
                distinct=False)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_random_config_sweep(seed):
+    """Seeded random configurations through the whole path against the
+    oracle: batch size, hidden size (FP8 needs a multiple of 128), expert
+    count, top-k (duplicates allowed in odd seeds), alignment, destination
+    count, COMPACT or FIXED capacity, BF16 or FP8, two-call or one-call
+    dispatch, masked and bad ids."""
+    rng = np.random.default_rng(900 + seed)
+    dispatch = "fp8" if rng.random() < 0.5 else "bf16"
+    H = int(rng.choice([128, 256, 384, 640, 1024, 2048]) if dispatch == "fp8"
+            else rng.choice([8, 72, 136, 256, 1000, 2056]))
+    E = int(rng.choice([1, 4, 8, 32, 64, 256]))
+    k = int(rng.integers(1, min(E, 9) + 1))
+    D = int(rng.choice([d for d in (1, 2, 4, 8) if E % d == 0]))
+    T = int(rng.integers(1, max(2, min(3000, 4_000_000 // H))))
+    mode = int(rng.random() < 0.3)
+    A = 1 if mode else int(rng.choice([1, 2, 16, 128]))
+    C = int(rng.choice([16, 64, 256])) if mode else 0
+    forward = bool(rng.random() < 0.5)
+    masked = float(rng.choice([0.0, 0.05]))
+    bad = float(rng.choice([0.0, 0.02]))
+    _run_small(T, H, E, k, A=A, D=D, C=C, mode=mode, seed=seed, masked=masked, bad=bad,
+               distinct=(seed % 2 == 0), dispatch=dispatch, forward=forward)
+
+
 def test_hot_experts():
     """Degenerate routing at sizes that take the multi-block layout: every
     token to the same k experts (one expert's count is T, the others 0),
