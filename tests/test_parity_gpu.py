@@ -245,6 +245,17 @@ def test_random_config_sweep(seed):
                distinct=(seed % 2 == 0), dispatch=dispatch, forward=forward)
 
 
+def test_widest_rows():
+    """The largest hidden size the configuration accepts (2^24 channels:
+    32 MiB BF16 rows, 16 MiB FP8 rows with 131,072 scales each) and a 2^20
+    one: every loop over a row runs thousands of passes and every in-row
+    byte offset exceeds 2^24; both dispatch kinds, two-call and one-call."""
+    _run_small(3, 1 << 24, 2, 1, A=2, seed=91)
+    _run_small(3, 1 << 24, 2, 1, A=2, seed=92, dispatch="fp8", forward=True)
+    _run_small(5, 1 << 20, 4, 2, A=2, D=2, seed=93, dispatch="fp8")
+    _run_small(5, 1 << 20, 4, 2, A=2, D=2, seed=94, forward=True, masked=0.2)
+
+
 def test_hot_experts():
     """Degenerate routing at sizes that take the multi-block layout: every
     token to the same k experts (one expert's count is T, the others 0),
