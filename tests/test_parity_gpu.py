@@ -256,6 +256,14 @@ def test_widest_rows():
     _run_small(5, 1 << 20, 4, 2, A=2, D=2, seed=94, forward=True, masked=0.2)
 
 
+def test_largest_batch():
+    """A million tokens at top-8 (8,388,608 pairs, 8,192 layout blocks: the
+    count matrix of 8,192 x 256 takes the separate scan kernel) with narrow
+    rows, FP8-free so the rows stay small: layout, dispatch and combine
+    against the oracle."""
+    _run_small(1 << 20, 8, 256, 8, A=128, D=8, seed=95, masked=0.01)
+
+
 def test_hot_experts():
     """Degenerate routing at sizes that take the multi-block layout: every
     token to the same k experts (one expert's count is T, the others 0),
